@@ -1,0 +1,236 @@
+"""Benchmark of the fused MoE-LoRA layer on one MI355X.
+
+One step = one full layer call (route, align, gate_up shrink, gate_up GEMM +
+expand + SiLU*up, down shrink, down GEMM + expand, top-k combine) on one
+batch of seeded synthetic input already resident in HBM.  Prints one JSON
+line with tokens/s, the roofline of the dominant kernel (timed live with
+HIP events on the stream it runs on) and the CPU oracle's rate on a bounded
+sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "MoE-LoRA layer tokens/s; achieved HBM GB/s (decode) / MFMA % of peak (prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense; f32 = vector peak
+STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
+DEFAULT_WORKLOAD = "decode_bf16"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=[w.name for w in synth.WORKLOADS])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lora_expert_gemm_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w, ids, aid):
+    """Bytes and FLOPs the method must move / compute for one call: weights of
+    the experts and (adapter, expert) pairs routed to, x read, out written;
+    FLOPs of the routed rows (padding and elementwise work excluded)."""
+    s = 2 if w.dtype == "bf16" else 4
+    T, H, I, k, r = w.T, w.H, w.I, w.k, w.r
+    valid = (ids >= 0) & (ids < w.E)
+    experts = np.unique(ids[valid])
+    tok_a = np.repeat(aid[:, None], k, axis=1)
+    lora_rows = valid & (tok_a >= 0) & (tok_a < w.NA)
+    pairs = np.unique(np.stack([tok_a[lora_rows], ids[lora_rows]], 1), axis=0) \
+        if lora_rows.any() else np.zeros((0, 2))
+    n_exp, n_pair, R, R_lora = len(experts), len(pairs), int(valid.sum()), int(lora_rows.sum())
+    layer_bytes = s * (n_exp * 3 * H * I + n_pair * r * (2 * H + 3 * I) + 2 * T * H)
+    layer_flop = R * 6 * H * I + R_lora * 2 * r * (2 * H + 3 * I)
+    # the dominant kernels: gate_up (base 2I x H per expert, expand 2I x r per
+    # pair, x in, h out, z in) and down (H x I per expert, H x r per pair, h in,
+    # y out)
+    gu_bytes = s * (n_exp * 2 * I * H + n_pair * 2 * I * r + T * H + R * I) + 4 * R_lora * r
+    gu_flop = R * 4 * H * I + R_lora * 4 * I * r
+    dn_bytes = s * (n_exp * H * I + n_pair * H * r + R * I) + 4 * R * H + 4 * R_lora * r
+    dn_flop = R * 2 * H * I + R_lora * 2 * H * r
+    return dict(n_exp=n_exp, n_pair=n_pair, R=R, R_lora=R_lora, layer_bytes=layer_bytes,
+                layer_flop=layer_flop, gate_up_bytes=gu_bytes, gate_up_flop=gu_flop,
+                down_bytes=dn_bytes, down_flop=dn_flop)
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 copies of {n} bytes")
+
+
+def cpu_baseline(w, d, target_s):
+    """The oracle (single thread, float64) on the first n tokens of the
+    workload, n chosen so that the run takes about target_s seconds."""
+    import oracle
+    dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+    ids, wts = oracle.ref_route(d["logits"], w.k)
+
+    def run(tokens):
+        t0 = time.perf_counter()
+        oracle.ref_forward(d["x"], ids, wts, d["adapter_ids"], d["W_gu"], d["W_d"],
+                           d["A_gu"], d["B_gu"], d["A_d"], d["B_d"], inter=w.I, rank=w.r,
+                           n_adapters=w.NA, dtype=dt, tokens=np.asarray(tokens, np.int32))
+        return time.perf_counter() - t0
+
+    t1 = run([0])
+    n = int(max(1, min(w.T, target_s / max(t1, 1e-6))))
+    el = run(list(range(n)))
+    return {"value": n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle (C, float64, 1 thread) on tokens 0..{n - 1} of {w.T} "
+                      f"of {w.name}; {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+            f"--gpus {args.gpus} is not supported")
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
+        return
+    import lora_expert_gemm_amd as L
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+    w = synth.workload(args.workload)
+    log(f"[bench] generating {w}")
+    d = synth.make_inputs(w)
+    dtype = L.BF16 if w.dtype == "bf16" else L.F32
+    plan = L.Plan(w.T, w.H, w.I, w.E, w.k, w.NA, w.r, dtype)
+    log(f"[bench] plan: {plan.info(w.T)}")
+
+    def dev(a):
+        a = a.view(np.int16) if a.dtype == np.uint16 else a
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    t = {n: dev(v) for n, v in d.items() if v is not None}
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.T, w.H), dtype=torch.int16 if w.dtype == "bf16" else torch.float32,
+                      device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.moelora_forward(plan.handle, w.T, t["x"], t["logits"], None, None, t["adapter_ids"],
+                          t["W_gu"], t["W_d"], t["A_gu"], t["B_gu"], t["A_d"], t["B_d"], out,
+                          ws, plan.workspace_bytes, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
+
+    # per-stage times: events recorded by the library around each kernel
+    # stage on the forward's own stream
+    L.moelora_timing_begin(plan.handle, args.steps)
+    for _ in range(args.steps):
+        step()
+    st_ms, n_calls = L.moelora_timing_end(plan.handle)
+    stage = {n: v / n_calls for n, v in zip(STAGES, st_ms)}
+    log("[bench] stages (ms/call): " + ", ".join(f"{n}={v:.4f}" for n, v in stage.items()))
+
+    lay = plan.layout(w.T)
+    torch.cuda.synchronize()
+    ids = ws[lay["off_topk_ids"]: lay["off_topk_ids"] + 4 * w.T * w.k].cpu().numpy() \
+        .view(np.int32).reshape(w.T, w.k)
+    alg = algorithmic(w, ids, d["adapter_ids"])
+
+    decode = w.T * w.k <= 24 * w.E
+    dom = max(("gate_up", "down"), key=lambda n: stage[n])
+    dom_s = stage[dom] / 1e3
+    if decode:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": alg[f"{dom}_bytes"] / dom_s / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "kernel": dom, "achieved": alg[f"{dom}_flop"] / dom_s / 1e12,
+                "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["launch_ms"] = stage[dom]
+    roof["units_per_launch"] = {"experts": alg["n_exp"], "adapter_expert_pairs": alg["n_pair"],
+                                "routed_rows": alg["R"]}
+
+    layer_s = ms / 1e3
+    res = {
+        "metric": METRIC,
+        "value": w.T / layer_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.k,
+                   "adapters": w.NA, "rank": w.r, "adapter_ids": w.adapters},
+        "roofline": roof,
+        "layer": {"algo_bytes": alg["layer_bytes"], "algo_flop": alg["layer_flop"],
+                  "GB/s": alg["layer_bytes"] / layer_s / 1e9,
+                  "TFLOP/s": alg["layer_flop"] / layer_s / 1e12,
+                  "hbm_frac": alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS},
+        "stages_ms": stage,
+        "plan": plan.info(w.T),
+        "kernel_source": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

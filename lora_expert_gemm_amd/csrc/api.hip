@@ -1,0 +1,418 @@
+// C ABI of the MoE-LoRA layer: plan, workspace layout, forward.
+//
+// The forward enqueues, on the caller's stream and without any host
+// synchronisation or allocation:
+//   route (only when logits are given) -> align (metadata + scatter) ->
+//   gate_up shrink -> gate_up GEMM + expand + SiLU*up -> down shrink ->
+//   down GEMM + expand -> top-k combine.
+// Grids are sized from upper bounds known on the host; blocks past the
+// device-side counts exit at once, so nothing waits for the device.  The
+// LoRA kernels are not launched at all when the call has no adapters (the
+// early exit of the AWS ML blog "Efficiently serve dozens of fine-tuned
+// models with vLLM on Amazon SageMaker AI and Amazon Bedrock", section
+// "Execution optimizations"), and nothing is compiled or specialised on the
+// token count (same section: recompiling per context length was the cause
+// of a tenfold time-to-first-token regression).
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "../../include/moelora.h"
+#include "kernels.h"
+
+using namespace moelora;
+
+struct moelora_plan_s {
+  moelora_desc d;
+  size_t ws_bytes;
+  // stage timing
+  bool timing = false;
+  int max_calls = 0, n_calls = 0;
+  std::vector<hipEvent_t> ev;  // (MOELORA_N_STAGES + 1) per call
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTgSmall = 1, kTgLarge = 4;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Token-count bucket: blocks of 16 rows while an expert gets about one
+// block of rows, else blocks of 64.
+int choose_tg(const moelora_desc &d, int T) {
+  const long long rows = (long long)T * d.top_k;
+  return rows <= 24LL * d.n_experts ? kTgSmall : kTgLarge;
+}
+
+// Workgroup K-splits of a shrink over contraction length K.
+int choose_split(int tg, int K) {
+  if (tg != kTgSmall) return 1;
+  return std::max(1, std::min(8, (K + 383) / 384));
+}
+
+struct Layout {
+  Shape s;
+  int split_gu, split_d, part_gu, part_d;
+  size_t off_error, off_counts, off_ids, off_w, off_sorted, off_bexp, off_seg, off_lseg,
+      off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_zgu, off_zd, off_h,
+      off_y, total;
+};
+
+Layout make_layout(const moelora_desc &d, int T) {
+  Layout L{};
+  Shape &s = L.s;
+  s.T = T;
+  s.H = d.hidden;
+  s.I = d.inter;
+  s.E = d.n_experts;
+  s.k = d.top_k;
+  s.NA = d.n_adapters;
+  s.r = d.rank;
+  s.R = T * d.top_k;
+  s.BM = 16 * choose_tg(d, T);
+  const long long ne = std::min<long long>(s.E, s.R);
+  const long long bound = (long long)s.R + ne * (s.BM - 1);
+  s.cap = (int)((bound + s.BM - 1) / s.BM * s.BM);
+  s.nblk = s.cap / s.BM;
+  s.max_seg = (int)std::min<long long>(s.R, (long long)s.E * s.NA);
+  s.max_tiles = s.nblk + s.max_seg;
+  const int tg = s.BM / 16;
+  L.split_gu = choose_split(tg, s.H);
+  L.split_d = choose_split(tg, s.I);
+  const int nks = s.r > 0 ? shrink_ksub(s.r) : 1;
+  L.part_gu = L.split_gu * nks;
+  L.part_d = L.split_d * nks;
+  const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
+  const size_t NB = (size_t)s.E * (s.NA + 1);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = up(o + bytes);
+    return at;
+  };
+  L.off_error = take(4);
+  L.off_counts = take(16);
+  L.off_ids = take(4ull * s.R);
+  L.off_w = take(4ull * s.R);
+  L.off_sorted = take(4ull * s.cap);
+  L.off_bexp = take(4ull * s.nblk);
+  L.off_seg = take(4ull * (s.E + 1));
+  L.off_lseg = take(16ull * s.max_seg);
+  L.off_tiles = take(16ull * s.max_tiles);
+  L.off_bts = take(4ull * (s.nblk + 1));
+  L.off_bcnt = take(4 * NB);
+  L.off_bbase = take(4 * NB);
+  L.off_tperm = take(4ull * T);
+  L.off_toff = take(4ull * (s.NA + 2));
+  L.off_zgu = take(4ull * L.part_gu * s.cap * s.r);
+  L.off_zd = take(4ull * L.part_d * s.cap * s.r);
+  L.off_h = take(es * s.cap * s.I);
+  L.off_y = take(4ull * s.R * s.H);
+  L.total = o;
+  return L;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moelora_status check_desc(const moelora_desc *d) {
+  if (!d) return MOELORA_ERR_INVALID_ARG;
+  if (d->flags != 0) return MOELORA_ERR_UNSUPPORTED;
+  if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
+  if (d->n_experts < 1 || d->n_experts > 1024) return MOELORA_ERR_UNSUPPORTED;
+  if (d->n_adapters < 0 || d->n_adapters > 255) return MOELORA_ERR_UNSUPPORTED;
+  if ((long long)d->n_experts * (d->n_adapters + 1) > 8448) return MOELORA_ERR_UNSUPPORTED;
+  if (d->top_k < 1 || d->top_k > std::min(d->n_experts, 32)) return MOELORA_ERR_UNSUPPORTED;
+  if (d->rank < 0 || d->rank > 256) return MOELORA_ERR_UNSUPPORTED;
+  if (d->n_adapters > 0 && d->rank < 1) return MOELORA_ERR_UNSUPPORTED;
+  if (d->hidden < 1 || d->hidden > 65536 || d->inter < 1 || d->inter > 65536)
+    return MOELORA_ERR_UNSUPPORTED;
+  if (d->max_tokens < 0 || (long long)d->max_tokens * d->top_k > (1LL << 24))
+    return MOELORA_ERR_UNSUPPORTED;
+  return MOELORA_OK;
+}
+
+GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora) {
+  GemmVariant v;
+  v.bf16 = d.dtype == MOELORA_BF16;
+  const int epc = v.bf16 ? 8 : 4;
+  const int ks = v.bf16 ? 32 : 16;
+  v.tg = tg;
+  v.vec = d.hidden % epc == 0 && d.inter % epc == 0 && (d.rank == 0 || d.rank % epc == 0);
+  v.even_k = v.vec && K % ks == 0;
+  v.lora = lora;
+  return v;
+}
+
+int k_tail(const moelora_desc &d, int K) {
+  const int ks = d.dtype == MOELORA_BF16 ? 32 : 16;
+  return (ks - K % ks) % ks;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moelora_status_string(moelora_status st) {
+  switch (st) {
+    case MOELORA_OK: return "ok";
+    case MOELORA_ERR_INVALID_ARG: return "invalid argument";
+    case MOELORA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOELORA_ERR_WORKSPACE: return "workspace too small";
+    case MOELORA_ERR_HIP: return "HIP runtime error";
+    case MOELORA_ERR_DEVICE: return "device error word set";
+  }
+  return "unknown status";
+}
+
+moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
+                            size_t *workspace_bytes) {
+  if (!plan || !workspace_bytes) return MOELORA_ERR_INVALID_ARG;
+  *plan = nullptr;
+  moelora_status st = check_desc(desc);
+  if (st != MOELORA_OK) return st;
+  moelora_plan_s *p = new (std::nothrow) moelora_plan_s();
+  if (!p) return MOELORA_ERR_INVALID_ARG;
+  p->d = *desc;
+  // the largest layout over every token count up to max_tokens: sizes grow
+  // with T inside a bucket, so the top of each bucket bounds it
+  size_t ws = make_layout(p->d, p->d.max_tokens).total;
+  int lo = 0, hi = p->d.max_tokens;
+  if (choose_tg(p->d, hi) != kTgSmall) {  // top of the small bucket
+    while (lo < hi) {
+      int mid = lo + (hi - lo + 1) / 2;
+      if (choose_tg(p->d, mid) == kTgSmall) lo = mid; else hi = mid - 1;
+    }
+    ws = std::max(ws, make_layout(p->d, lo).total);
+  }
+  p->ws_bytes = ws;
+  *plan = p;
+  *workspace_bytes = ws;
+  return MOELORA_OK;
+}
+
+void moelora_plan_destroy(moelora_plan_t plan) {
+  if (!plan) return;
+  for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
+  delete plan;
+}
+
+moelora_status moelora_workspace_layout(moelora_plan_t plan, int32_t n_tokens,
+                                        moelora_layout *out) {
+  if (!plan || !out || n_tokens < 0 || n_tokens > plan->d.max_tokens)
+    return MOELORA_ERR_INVALID_ARG;
+  const Layout L = make_layout(plan->d, n_tokens);
+  memset(out, 0, sizeof *out);
+  out->block_m = L.s.BM;
+  out->cap = L.s.cap;
+  out->nblk = L.s.nblk;
+  out->max_seg = L.s.max_seg;
+  out->max_tiles = L.s.max_tiles;
+  out->off_topk_ids = L.off_ids;
+  out->off_topk_w = L.off_w;
+  out->off_sorted_rows = L.off_sorted;
+  out->off_block_expert = L.off_bexp;
+  out->off_seg_start = L.off_seg;
+  out->off_lora_seg = L.off_lseg;
+  out->off_tiles = L.off_tiles;
+  out->off_block_tile_start = L.off_bts;
+  out->off_counts = L.off_counts;
+  out->off_error = L.off_error;
+  return MOELORA_OK;
+}
+
+moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *buf,
+                                 size_t buf_len) {
+  if (!plan || !buf || buf_len == 0 || n_tokens < 0 || n_tokens > plan->d.max_tokens)
+    return MOELORA_ERR_INVALID_ARG;
+  const moelora_desc &d = plan->d;
+  const Layout L = make_layout(d, n_tokens);
+  const int tg = L.s.BM / 16;
+  const GemmVariant vg = variant(d, tg, d.hidden, true), vd = variant(d, tg, d.inter, true);
+  snprintf(buf, buf_len,
+           "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
+           "k_tail_d=%d split_gu=%d split_d=%d partials_gu=%d partials_d=%d cap=%d "
+           "workspace=%zu",
+           vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
+           k_tail(d, d.hidden), k_tail(d, d.inter), L.split_gu, L.split_d, L.part_gu, L.part_d,
+           L.s.cap, L.total);
+  return MOELORA_OK;
+}
+
+moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void *x,
+                               const float *router_logits, const int32_t *topk_ids,
+                               const float *topk_w, const int32_t *adapter_ids,
+                               const void *w_gate_up, const void *w_down, const void *lora_a_gu,
+                               const void *lora_b_gu, const void *lora_a_d, const void *lora_b_d,
+                               void *out, void *workspace, size_t workspace_bytes,
+                               moelora_stream_t stream) {
+  if (!plan) return MOELORA_ERR_INVALID_ARG;
+  const moelora_desc &d = plan->d;
+  if (n_tokens < 0 || n_tokens > d.max_tokens) return MOELORA_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOELORA_OK;
+  if (!x || !w_gate_up || !w_down || !out || !workspace) return MOELORA_ERR_INVALID_ARG;
+  // exactly one routing source: logits, or caller ids with their weights
+  const bool own_route = topk_ids == nullptr;
+  if (own_route ? (!router_logits || topk_w) : (!topk_w || router_logits))
+    return MOELORA_ERR_INVALID_ARG;
+  const int n_lora_ptr = !!lora_a_gu + !!lora_b_gu + !!lora_a_d + !!lora_b_d;
+  if (n_lora_ptr != 0 && n_lora_ptr != 4) return MOELORA_ERR_INVALID_ARG;
+  const bool lora = n_lora_ptr == 4 && adapter_ids && d.n_adapters > 0 && d.rank > 0;
+  const void *ptrs16[] = {x, w_gate_up, w_down, out, lora_a_gu, lora_b_gu, lora_a_d, lora_b_d};
+  for (const void *p : ptrs16)
+    if (p && !aligned(p, 16)) return MOELORA_ERR_INVALID_ARG;
+  if (!aligned(workspace, kAlign)) return MOELORA_ERR_INVALID_ARG;
+
+  const Layout L = make_layout(d, n_tokens);
+  if (workspace_bytes < L.total || L.total > plan->ws_bytes) return MOELORA_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const Shape &s = L.s;
+  const int tg = s.BM / 16;
+
+  AlignBufs al;
+  al.sorted_rows = reinterpret_cast<int *>(ws + L.off_sorted);
+  al.block_expert = reinterpret_cast<int *>(ws + L.off_bexp);
+  al.seg_start = reinterpret_cast<int *>(ws + L.off_seg);
+  al.lora_seg = reinterpret_cast<int *>(ws + L.off_lseg);
+  al.tiles = reinterpret_cast<int *>(ws + L.off_tiles);
+  al.block_tile_start = reinterpret_cast<int *>(ws + L.off_bts);
+  al.counts = reinterpret_cast<int *>(ws + L.off_counts);
+  al.error = reinterpret_cast<int *>(ws + L.off_error);
+  al.bucket_cnt = reinterpret_cast<int *>(ws + L.off_bcnt);
+  al.bucket_base = reinterpret_cast<int *>(ws + L.off_bbase);
+  al.tok_perm = reinterpret_cast<int *>(ws + L.off_tperm);
+  al.tok_off = reinterpret_cast<int *>(ws + L.off_toff);
+
+  hipEvent_t *ev = nullptr;
+  if (plan->timing && plan->n_calls < plan->max_calls)
+    ev = &plan->ev[(size_t)plan->n_calls++ * (MOELORA_N_STAGES + 1)];
+  int stage = 0;
+  auto mark = [&]() -> hipError_t {
+    return ev ? hipEventRecord(ev[stage++], st) : hipSuccess;
+  };
+#define MOELORA_TRY(expr)                    \
+  do {                                       \
+    if ((expr) != hipSuccess) return MOELORA_ERR_HIP; \
+  } while (0)
+
+  MOELORA_TRY(mark());
+  const int *ids = topk_ids;
+  const float *wts = topk_w;
+  if (own_route) {
+    int *ids_ws = reinterpret_cast<int *>(ws + L.off_ids);
+    float *w_ws = reinterpret_cast<float *>(ws + L.off_w);
+    MOELORA_TRY(launch_route(router_logits, s.T, s.E, s.k, ids_ws, w_ws, st));
+    ids = ids_ws;
+    wts = w_ws;
+  }
+  MOELORA_TRY(mark());
+  MOELORA_TRY(launch_align(s, ids, lora ? adapter_ids : nullptr, al, st));
+  MOELORA_TRY(mark());
+
+  GemmArgs g{};
+  g.s = s;
+  g.topk_ids = ids;
+  g.x = x;
+  g.al = al;
+  g.h = ws + L.off_h;
+  g.y = reinterpret_cast<float *>(ws + L.off_y);
+  float *z_gu = reinterpret_cast<float *>(ws + L.off_zgu);
+  float *z_d = reinterpret_cast<float *>(ws + L.off_zd);
+
+  if (lora) {
+    GemmArgs a = g;
+    a.A = lora_a_gu;
+    a.z_out = z_gu;
+    a.split = L.split_gu;
+    MOELORA_TRY(launch_shrink(a, variant(d, tg, d.hidden, true), false, st));
+  }
+  MOELORA_TRY(mark());
+  {
+    GemmArgs a = g;
+    a.W = w_gate_up;
+    a.B = lora_b_gu;
+    a.z = z_gu;
+    a.n_part = L.part_gu;
+    MOELORA_TRY(launch_gate_up(a, variant(d, tg, d.hidden, lora), st));
+  }
+  MOELORA_TRY(mark());
+  if (lora) {
+    GemmArgs a = g;
+    a.A = lora_a_d;
+    a.z_out = z_d;
+    a.split = L.split_d;
+    MOELORA_TRY(launch_shrink(a, variant(d, tg, d.inter, true), true, st));
+  }
+  MOELORA_TRY(mark());
+  {
+    GemmArgs a = g;
+    a.W = w_down;
+    a.B = lora_b_d;
+    a.z = z_d;
+    a.n_part = L.part_d;
+    MOELORA_TRY(launch_down(a, variant(d, tg, d.inter, lora), st));
+  }
+  MOELORA_TRY(mark());
+  MOELORA_TRY(launch_combine(s, ids, wts, g.y, out, d.dtype == MOELORA_BF16, st));
+  MOELORA_TRY(mark());
+#undef MOELORA_TRY
+  return MOELORA_OK;
+}
+
+moelora_status moelora_read_device_error(moelora_plan_t plan, const void *workspace,
+                                         int32_t *error_bits, moelora_stream_t stream) {
+  if (!plan || !workspace || !error_bits) return MOELORA_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return MOELORA_ERR_HIP;
+  const Layout L = make_layout(plan->d, 0);
+  if (hipMemcpy(error_bits, static_cast<const char *>(workspace) + L.off_error, 4,
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return MOELORA_ERR_HIP;
+  return MOELORA_OK;
+}
+
+moelora_status moelora_timing_begin(moelora_plan_t plan, int32_t max_calls) {
+  if (!plan || max_calls < 1 || plan->timing) return MOELORA_ERR_INVALID_ARG;
+  plan->ev.assign((size_t)max_calls * (MOELORA_N_STAGES + 1), nullptr);
+  for (hipEvent_t &e : plan->ev)
+    if (hipEventCreate(&e) != hipSuccess) return MOELORA_ERR_HIP;
+  plan->timing = true;
+  plan->max_calls = max_calls;
+  plan->n_calls = 0;
+  return MOELORA_OK;
+}
+
+moelora_status moelora_timing_end(moelora_plan_t plan, double *stage_ms, int32_t n_stages,
+                                  int32_t *n_calls) {
+  if (!plan || !plan->timing || !stage_ms || n_stages < 0 || !n_calls)
+    return MOELORA_ERR_INVALID_ARG;
+  moelora_status rc = MOELORA_OK;
+  for (int i = 0; i < n_stages; ++i) stage_ms[i] = 0.0;
+  for (int c = 0; c < plan->n_calls && rc == MOELORA_OK; ++c) {
+    hipEvent_t *ev = &plan->ev[(size_t)c * (MOELORA_N_STAGES + 1)];
+    if (hipEventSynchronize(ev[MOELORA_N_STAGES]) != hipSuccess) {
+      rc = MOELORA_ERR_HIP;
+      break;
+    }
+    for (int i = 0; i < std::min(n_stages, (int)MOELORA_N_STAGES); ++i) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) {
+        rc = MOELORA_ERR_HIP;
+        break;
+      }
+      stage_ms[i] += ms;
+    }
+  }
+  *n_calls = plan->n_calls;
+  for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
+  plan->ev.clear();
+  plan->timing = false;
+  plan->max_calls = plan->n_calls = 0;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Kernel arguments and host-side launchers of the MoE-LoRA layer kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moelora.h"
+
+namespace moelora {
+
+// Shape of one forward call (token-count dependent parts included).
+struct Shape {
+  int T, H, I, E, k, NA, r;
+  int R;      // T * k routed rows
+  int BM;     // rows per block (a multiple of 16)
+  int cap;    // upper bound of the padded row count
+  int nblk;   // cap / BM
+  int max_seg, max_tiles;
+};
+
+// Alignment arrays in the workspace.
+struct AlignBufs {
+  int *sorted_rows;       // [cap]
+  int *block_expert;      // [nblk]
+  int *seg_start;         // [E + 1]
+  int *lora_seg;          // [max_seg][4]
+  int *tiles;             // [max_tiles][4]
+  int *block_tile_start;  // [nblk + 1]
+  int *counts;            // [4]: num_padded, n_lora_seg, n_tiles, 0
+  int *error;             // [1]
+  int *bucket_cnt;        // [E][NA + 1] rows per (expert, adapter rank)
+  int *bucket_base;       // [E][NA + 1] first sorted position of the bucket
+  int *tok_perm;          // [T] tokens ordered by (adapter rank, token)
+  int *tok_off;           // [NA + 2] start of each adapter rank in tok_perm
+};
+
+// Operands of the expert GEMM kernels.  Pointers are typed void and cast to
+// the element type inside the templates.
+struct GemmArgs {
+  Shape s;
+  const int *topk_ids;     // [R]
+  const void *x;           // [T][H]
+  const void *W;           // base weights of this projection
+  const void *A;           // LoRA A of this projection (shrink kernels)
+  const void *B;           // LoRA B of this projection (expand epilogue)
+  const float *z;          // [P][cap][r] shrink partials read by the expand
+  float *z_out;            // [P][cap][r] shrink partials written
+  int n_part;              // P: partials to sum
+  int split;               // workgroup K-splits of the shrink kernels
+  void *h;                 // [cap][I] SiLU(gate)*up, layer dtype
+  float *y;                // [R][H] down output per routed row
+  AlignBufs al;
+};
+
+// Number of workgroups along the weight-row axis of the GEMM kernels: each
+// covers 64 output columns (4 waves x 16).
+constexpr int kColsPerWg = 64;
+
+// Shrink kernels: partial sums per workgroup split; each of the 4 waves
+// takes one 16-row group of A and one of `ks` K sub-ranges.
+__host__ __device__ inline int shrink_ksub(int r) {
+  int ncg = (r + 15) / 16;
+  return ncg >= 4 ? 1 : 4 / ncg;
+}
+
+// Launchers (return hipGetLastError()).
+hipError_t launch_route(const float *logits, int T, int E, int k, int *ids, float *w,
+                        hipStream_t st);
+hipError_t launch_align(const Shape &s, const int *ids, const int *adapter_ids,
+                        const AlignBufs &al, hipStream_t st);
+
+struct GemmVariant {
+  bool bf16;     // element type
+  int tg;        // 16-row token groups per block (BM = 16 * tg)
+  bool vec;      // 16-byte vector loads allowed
+  bool even_k;   // contraction length a multiple of the K step
+  bool lora;     // expand epilogue on
+};
+hipError_t launch_gate_up(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
+hipError_t launch_down(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
+hipError_t launch_shrink(const GemmArgs &a, const GemmVariant &v, bool from_h, hipStream_t st);
+hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const float *y,
+                          void *out, bool bf16, hipStream_t st);
+
+}  // namespace moelora
