@@ -196,13 +196,13 @@ MOELORA_API moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_toke
  * plan records HIP events around each stage of every forward (at most
  * max_calls forwards), on the forward's stream.  moelora_timing_end
  * synchronises, writes the summed milliseconds of each stage into
- * stage_ms[0..n_stages) (stages: 0 route, 1 align, 2 gate_up shrink,
- * 3 gate_up GEMM + expand + SiLU*up, 4 down shrink, 5 down GEMM + expand,
- * 6 top-k combine) and the number of timed forwards into *n_calls.  Events
+ * stage_ms[0..n_stages) (stages: 0 routing + alignment, 1 gate_up shrink,
+ * 2 gate_up GEMM + expand + SiLU*up, 3 down shrink, 4 down GEMM + expand,
+ * 5 top-k combine) and the number of timed forwards into *n_calls.  Events
  * are created in begin and destroyed in end, so timed forwards still
  * allocate nothing.  A plan in timing mode must not be used from two
  * threads at once. */
-#define MOELORA_N_STAGES 7
+#define MOELORA_N_STAGES 6
 MOELORA_API moelora_status moelora_timing_begin(moelora_plan_t plan, int32_t max_calls);
 MOELORA_API moelora_status moelora_timing_end(moelora_plan_t plan, double *stage_ms,
                                   int32_t n_stages, int32_t *n_calls);

@@ -28,8 +28,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 DEVERR_EXPERT_ID, DEVERR_ADAPTER_ID = 1, 2
-N_STAGES = 7
-STAGES = ("route", "align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
+N_STAGES = 6
+STAGES = ("route_align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
 
 class moelora_desc(ctypes.Structure):

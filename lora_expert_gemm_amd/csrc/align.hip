@@ -24,6 +24,7 @@ constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kMaxBuckets = 8448;   // E * (NA + 1)
 constexpr int kMaxAdapterRanks = 256;  // NA + 1
 constexpr int kScatterThreads = 512;
+constexpr int kSmallRows = kAlignThreads / 4;  // fused route + align up to this many rows
 
 __device__ __forceinline__ unsigned long long lanemask_lt(int lane) {
   return (1ull << lane) - 1ull;
@@ -53,41 +54,74 @@ __device__ int block_excl_scan(int v, int *tmp, int *total) {
   return off + x - v;
 }
 
-// Router: per token, the k largest logits (ties to the lower expert index,
-// largest first) and their softmax over the kept logits.  One thread per
-// token; round j takes the best logit ordered after round j-1's pick in the
-// order (descending value, ascending index), so no "taken" set is needed.
+// Router for one token, computed by one wave: the k largest logits (ties to
+// the lower expert index, largest first) and their softmax over the kept
+// logits.  Lane l holds experts l, l + 64, ...; each of the k rounds takes
+// the wave-wide best untaken (value, index) by a butterfly reduction.  Lanes
+// j < k end with the j-th pick in (*id, *wt).
+constexpr int kRouteMaxPerLane = 1024 / kWave;
+
+__device__ void route_token(const float *__restrict__ row, int E, int k, int *id, float *wt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (E + kWave - 1) / kWave;
+  float v[kRouteMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kRouteMaxPerLane; ++i) {
+    const int e = lane + i * kWave;
+    v[i] = (i < per && e < E) ? row[e] : -__builtin_inff();
+  }
+  unsigned taken = 0;  // bit i: expert lane + 64 i already chosen
+  float my_val = 0.f, top = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kRouteMaxPerLane; ++i) {
+      const int e = lane + i * kWave;
+      if (i < per && e < E && !(taken >> i & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d);
+      const int oi = __shfl_xor(bi, d);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (j == 0) top = bv;
+    if (lane == j) {
+      my_val = bv;
+      my_id = bi;
+    }
+  }
+  const float ex = lane < k ? expf(my_val - top) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  *id = my_id;
+  *wt = ex / sum;
+}
+
+// One wave per token.
 __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E,
                                                int k, int *__restrict__ ids,
                                                float *__restrict__ w) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
-  const float *row = logits + (size_t)t * E;
-  float pv = __builtin_inff();
-  int pi = -1;
-  float top = 0.f;
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j) {
-    int best = -1;
-    float bv = 0.f;
-    for (int e = 0; e < E; ++e) {
-      const float l = row[e];
-      const bool after = (l < pv) || (l == pv && e > pi);
-      if (after && (best < 0 || l > bv)) {
-        best = e;
-        bv = l;
-      }
-    }
-    ids[(size_t)t * k + j] = best;
-    if (j == 0) top = bv;
-    const float ex = expf(bv - top);
-    w[(size_t)t * k + j] = ex;
-    sum += ex;
-    pv = bv;
-    pi = best;
+  int id;
+  float wt;
+  route_token(logits + (size_t)t * E, E, k, &id, &wt);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
   }
-  const float inv = 1.0f / sum;
-  for (int j = 0; j < k; ++j) w[(size_t)t * k + j] *= inv;
 }
 
 __device__ __forceinline__ int adapter_rank(const int *aid, int t, int NA, int &err) {
@@ -97,46 +131,20 @@ __device__ __forceinline__ int adapter_rank(const int *aid, int t, int NA, int &
   return (a >= 0 && a < NA) ? a : NA;
 }
 
-// Alignment metadata, one workgroup: bucket histogram, padded expert
-// segments, per-bucket start positions, padding sentinels, block experts,
-// LoRA segments and tiles, and the tokens ordered by adapter rank.
-__global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int *__restrict__ ids,
-                                                              const int *__restrict__ aid,
-                                                              AlignBufs al) {
-  __shared__ int hist[kMaxBuckets];
-  __shared__ int seg[1024 + 1];
-  __shared__ int scan_tmp[kAlignWaves];
-  __shared__ int tok_cnt[kMaxAdapterRanks];
-  __shared__ int tok_base[kMaxAdapterRanks];
-  __shared__ int cursor[kMaxAdapterRanks];
-  __shared__ int wtab[kAlignWaves][kMaxAdapterRanks];
+struct AlignSmem {
+  int hist[kMaxBuckets];  // rows per (expert, adapter rank) bucket
+  int seg[1024 + 1];      // padded expert starts
+  int scan_tmp[kAlignWaves];
+};
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, R = s.R, k = s.k, T = s.T;
-  const int NB = E * NR;
-
-  for (int i = tid; i < NB; i += kAlignThreads) hist[i] = 0;
-  for (int i = tid; i < NR; i += kAlignThreads) {
-    tok_cnt[i] = 0;
-    cursor[i] = 0;
-  }
-  for (int i = tid; i < kAlignWaves * NR; i += kAlignThreads) wtab[i / NR][i % NR] = 0;
-  if (tid == 0) *al.error = 0;
-  __syncthreads();
-
-  int err = 0;
-  for (int t = tid; t < T; t += kAlignThreads) atomicAdd(&tok_cnt[adapter_rank(aid, t, NA, err)], 1);
-  for (int p = tid; p < R; p += kAlignThreads) {
-    const int e = ids[p];
-    if (e < 0 || e >= E) {
-      err |= MOELORA_DEVERR_EXPERT_ID;
-      continue;
-    }
-    int dummy = 0;
-    atomicAdd(&hist[e * NR + adapter_rank(aid, p / k, NA, dummy)], 1);
-  }
-  if (err) atomicOr(al.error, err);
-  __syncthreads();
+// Everything that follows from the bucket histogram (in LDS): padded expert
+// segments, bucket start positions (al.bucket_base / bucket_cnt), padding
+// sentinels, block experts, LoRA segments and their block tiles, the first
+// tile of every block, and the counts.  All 1024 threads call it.
+__device__ void align_layout(const Shape &s, AlignSmem &sm, const AlignBufs &al) {
+  const int tid = threadIdx.x;
+  const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, R = s.R;
+  int *hist = sm.hist, *seg = sm.seg;
 
   // padded expert segments (E <= 1024: one expert per thread)
   int padded = 0;
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
     padded = (c + BM - 1) / BM * BM;
   }
   int num_padded;
-  const int excl = block_excl_scan(padded, scan_tmp, &num_padded);
+  const int excl = block_excl_scan(padded, sm.scan_tmp, &num_padded);
   if (tid < E) seg[tid] = excl;
   if (tid == 0) seg[E] = num_padded;
   __syncthreads();
@@ -183,15 +191,14 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
     }
   }
   int n_seg, n_tiles;
-  int seg_i = block_excl_scan(my_seg, scan_tmp, &n_seg);
-  int tile_i = block_excl_scan(my_tiles, scan_tmp, &n_tiles);
+  int seg_i = block_excl_scan(my_seg, sm.scan_tmp, &n_seg);
+  int tile_i = block_excl_scan(my_tiles, sm.scan_tmp, &n_tiles);
   for (int f = f0; f < f1; ++f) {
     const int e = f / NA, a = f % NA, b = e * NR + a;
     const int c = hist[b];
     if (c <= 0) continue;
     const int st = al.bucket_base[b], en = st + c;
-    int4 *sg = reinterpret_cast<int4 *>(al.lora_seg) + seg_i++;
-    *sg = make_int4(e, a, st, c);
+    reinterpret_cast<int4 *>(al.lora_seg)[seg_i++] = make_int4(e, a, st, c);
     for (int blk = st / BM; blk <= (en - 1) / BM; ++blk) {
       const int lo = max(st, blk * BM), hi = min(en, (blk + 1) * BM);
       reinterpret_cast<int4 *>(al.tiles)[tile_i++] = make_int4(blk, a, lo - blk * BM, hi - lo);
@@ -217,6 +224,50 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
     al.counts[1] = n_seg;
     al.counts[2] = n_tiles;
     al.counts[3] = 0;
+  }
+}
+
+// Alignment metadata for any batch, one workgroup: bucket histogram, then
+// align_layout, then the tokens ordered by adapter rank (for the scatter).
+__global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int *__restrict__ ids,
+                                                              const int *__restrict__ aid,
+                                                              AlignBufs al) {
+  __shared__ AlignSmem sm;
+  __shared__ int tok_cnt[kMaxAdapterRanks];
+  __shared__ int tok_base[kMaxAdapterRanks];
+  __shared__ int cursor[kMaxAdapterRanks];
+  __shared__ int wtab[kAlignWaves][kMaxAdapterRanks];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int E = s.E, NA = s.NA, NR = NA + 1, R = s.R, k = s.k, T = s.T;
+  const int NB = E * NR;
+
+  for (int i = tid; i < NB; i += kAlignThreads) sm.hist[i] = 0;
+  for (int i = tid; i < NR; i += kAlignThreads) {
+    tok_cnt[i] = 0;
+    cursor[i] = 0;
+  }
+  for (int i = tid; i < kAlignWaves * NR; i += kAlignThreads) wtab[i / NR][i % NR] = 0;
+  if (tid == 0) *al.error = 0;
+  __syncthreads();
+
+  int err = 0;
+  for (int t = tid; t < T; t += kAlignThreads) atomicAdd(&tok_cnt[adapter_rank(aid, t, NA, err)], 1);
+  for (int p = tid; p < R; p += kAlignThreads) {
+    const int e = ids[p];
+    if (e < 0 || e >= E) {
+      err |= MOELORA_DEVERR_EXPERT_ID;
+      continue;
+    }
+    int dummy = 0;
+    atomicAdd(&sm.hist[e * NR + adapter_rank(aid, p / k, NA, dummy)], 1);
+  }
+  if (err) atomicOr(al.error, err);
+  __syncthreads();
+
+  align_layout(s, sm, al);
+
+  if (tid == 0) {
     int run = 0;
     for (int a = 0; a < NR; ++a) {
       tok_base[a] = run;
@@ -304,17 +355,81 @@ __global__ __launch_bounds__(kScatterThreads) void k_align_scatter(Shape s,
   }
 }
 
-}  // namespace
+// Small batches (R <= kSmallRows routed rows): routing and the whole
+// alignment in one workgroup.  Rows are ranked inside their bucket by
+// counting the earlier rows with the same key (R comparisons from LDS per
+// row), which yields the same stable order as the two-kernel path.
+__global__ __launch_bounds__(kAlignThreads) void k_route_align_small(
+    Shape s, const float *__restrict__ logits, const int *__restrict__ ids_in,
+    int *__restrict__ ids_out, float *__restrict__ w_out, const int *__restrict__ aid,
+    AlignBufs al) {
+  __shared__ AlignSmem sm;
+  __shared__ int key[kSmallRows];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int E = s.E, NA = s.NA, NR = NA + 1, R = s.R, k = s.k, T = s.T;
+  const int NB = E * NR;
 
-hipError_t launch_route(const float *logits, int T, int E, int k, int *ids, float *w,
-                        hipStream_t st) {
-  if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route, dim3((T + 255) / 256), dim3(256), 0, st, logits, T, E, k, ids, w);
-  return hipGetLastError();
+  if (logits) {
+    for (int t = wv; t < T; t += kAlignWaves) {
+      int id;
+      float wt;
+      route_token(logits + (size_t)t * E, E, k, &id, &wt);
+      if (lane < k) {
+        ids_out[t * k + lane] = id;
+        w_out[t * k + lane] = wt;
+        key[t * k + lane] = id;
+      }
+    }
+  } else {
+    for (int p = tid; p < R; p += kAlignThreads) key[p] = ids_in[p];
+  }
+  for (int i = tid; i < NB; i += kAlignThreads) sm.hist[i] = 0;
+  if (tid == 0) *al.error = 0;
+  __syncthreads();
+
+  // key = expert * (NA + 1) + adapter rank, or -1 for a dropped row
+  int err = 0;
+  int my_key = -1;
+  if (tid < R) {
+    const int e = key[tid];
+    const int ar = adapter_rank(aid, tid / k, NA, err);
+    if (e < 0 || e >= E) {
+      err |= MOELORA_DEVERR_EXPERT_ID;
+    } else {
+      my_key = e * NR + ar;
+      atomicAdd(&sm.hist[my_key], 1);
+    }
+  }
+  if (err) atomicOr(al.error, err);
+  __syncthreads();
+  if (tid < R) key[tid] = my_key;
+
+  align_layout(s, sm, al);  // contains barriers: key[] is visible after it
+
+  if (my_key >= 0) {
+    int rank = 0;
+    for (int q = 0; q < tid; ++q) rank += key[q] == my_key;
+    al.sorted_rows[al.bucket_base[my_key] + rank] = tid;
+  }
 }
 
-hipError_t launch_align(const Shape &s, const int *ids, const int *adapter_ids,
-                        const AlignBufs &al, hipStream_t st) {
+}  // namespace
+
+hipError_t launch_route_align(const Shape &s, const float *logits, const int *ids,
+                              int *ids_ws, float *w_ws, const int *adapter_ids,
+                              const AlignBufs &al, hipStream_t st) {
+  if (s.R <= kSmallRows) {
+    hipLaunchKernelGGL(k_route_align_small, dim3(1), dim3(kAlignThreads), 0, st, s, logits, ids,
+                       ids_ws, w_ws, adapter_ids, al);
+    return hipGetLastError();
+  }
+  if (logits) {
+    hipLaunchKernelGGL(k_route, dim3((s.T + 3) / 4), dim3(256), 0, st, logits, s.T, s.E, s.k,
+                       ids_ws, w_ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ids = ids_ws;
+  }
   hipLaunchKernelGGL(k_align_meta, dim3(1), dim3(kAlignThreads), 0, st, s, ids, adapter_ids, al);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

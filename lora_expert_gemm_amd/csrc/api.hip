@@ -14,6 +14,7 @@
 // token count (same section: recompiling per context length was the cause
 // of a tenfold time-to-first-token regression).
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -28,6 +29,7 @@ using namespace moelora;
 struct moelora_plan_s {
   moelora_desc d;
   size_t ws_bytes;
+  int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -48,15 +50,17 @@ int choose_tg(const moelora_desc &d, int T) {
   return rows <= 24LL * d.n_experts ? kTgSmall : kTgLarge;
 }
 
-// Workgroup K-splits of a shrink over contraction length K.
-int choose_split(int tg, int K) {
-  if (tg != kTgSmall) return 1;
-  return std::max(1, std::min(8, (K + 383) / 384));
+// Waves (16 output columns each) per GEMM workgroup.  The decode weight
+// stream wants thousands of small workgroups: 64 weight rows per workgroup
+// (gate_up: 2 waves x (16 gate + 16 up) rows; down: 4 waves x 16 rows).
+int choose_waves(int tg, bool gate_up) {
+  if (tg == kTgSmall) return gate_up ? 2 : 4;
+  return 4;
 }
 
 struct Layout {
   Shape s;
-  int split_gu, split_d, part_gu, part_d;
+  int waves_gu, waves_d;
   size_t off_error, off_counts, off_ids, off_w, off_sorted, off_bexp, off_seg, off_lseg,
       off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_zgu, off_zd, off_h,
       off_y, total;
@@ -81,11 +85,8 @@ Layout make_layout(const moelora_desc &d, int T) {
   s.max_seg = (int)std::min<long long>(s.R, (long long)s.E * s.NA);
   s.max_tiles = s.nblk + s.max_seg;
   const int tg = s.BM / 16;
-  L.split_gu = choose_split(tg, s.H);
-  L.split_d = choose_split(tg, s.I);
-  const int nks = s.r > 0 ? shrink_ksub(s.r) : 1;
-  L.part_gu = L.split_gu * nks;
-  L.part_d = L.split_d * nks;
+  L.waves_gu = choose_waves(tg, true);
+  L.waves_d = choose_waves(tg, false);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
   const size_t NB = (size_t)s.E * (s.NA + 1);
   size_t o = 0;
@@ -108,8 +109,8 @@ Layout make_layout(const moelora_desc &d, int T) {
   L.off_bbase = take(4 * NB);
   L.off_tperm = take(4ull * T);
   L.off_toff = take(4ull * (s.NA + 2));
-  L.off_zgu = take(4ull * L.part_gu * s.cap * s.r);
-  L.off_zd = take(4ull * L.part_d * s.cap * s.r);
+  L.off_zgu = take(4ull * s.cap * s.r);
+  L.off_zd = take(4ull * s.cap * s.r);
   L.off_h = take(es * s.cap * s.I);
   L.off_y = take(4ull * s.R * s.H);
   L.total = o;
@@ -189,6 +190,9 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
     ws = std::max(ws, make_layout(p->d, lo).total);
   }
   p->ws_bytes = ws;
+  // tuning sweeps only: force the waves per GEMM workgroup (1..4)
+  if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
+  if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -232,13 +236,13 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   const Layout L = make_layout(d, n_tokens);
   const int tg = L.s.BM / 16;
   const GemmVariant vg = variant(d, tg, d.hidden, true), vd = variant(d, tg, d.inter, true);
+  const int wgu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
+  const int wd = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
   snprintf(buf, buf_len,
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
-           "k_tail_d=%d split_gu=%d split_d=%d partials_gu=%d partials_d=%d cap=%d "
-           "workspace=%zu",
+           "k_tail_d=%d waves_gu=%d waves_d=%d shrink_waves=%d cap=%d workspace=%zu",
            vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
-           k_tail(d, d.hidden), k_tail(d, d.inter), L.split_gu, L.split_d, L.part_gu, L.part_d,
-           L.s.cap, L.total);
+           k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, kShrinkWaves, L.s.cap, L.total);
   return MOELORA_OK;
 }
 
@@ -300,17 +304,12 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   } while (0)
 
   MOELORA_TRY(mark());
-  const int *ids = topk_ids;
-  const float *wts = topk_w;
-  if (own_route) {
-    int *ids_ws = reinterpret_cast<int *>(ws + L.off_ids);
-    float *w_ws = reinterpret_cast<float *>(ws + L.off_w);
-    MOELORA_TRY(launch_route(router_logits, s.T, s.E, s.k, ids_ws, w_ws, st));
-    ids = ids_ws;
-    wts = w_ws;
-  }
-  MOELORA_TRY(mark());
-  MOELORA_TRY(launch_align(s, ids, lora ? adapter_ids : nullptr, al, st));
+  int *ids_ws = reinterpret_cast<int *>(ws + L.off_ids);
+  float *w_ws = reinterpret_cast<float *>(ws + L.off_w);
+  MOELORA_TRY(launch_route_align(s, own_route ? router_logits : nullptr, topk_ids, ids_ws, w_ws,
+                                 lora ? adapter_ids : nullptr, al, st));
+  const int *ids = own_route ? ids_ws : topk_ids;
+  const float *wts = own_route ? w_ws : topk_w;
   MOELORA_TRY(mark());
 
   GemmArgs g{};
@@ -327,7 +326,6 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     GemmArgs a = g;
     a.A = lora_a_gu;
     a.z_out = z_gu;
-    a.split = L.split_gu;
     MOELORA_TRY(launch_shrink(a, variant(d, tg, d.hidden, true), false, st));
   }
   MOELORA_TRY(mark());
@@ -336,7 +334,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.W = w_gate_up;
     a.B = lora_b_gu;
     a.z = z_gu;
-    a.n_part = L.part_gu;
+    a.waves = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
     MOELORA_TRY(launch_gate_up(a, variant(d, tg, d.hidden, lora), st));
   }
   MOELORA_TRY(mark());
@@ -344,7 +342,6 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     GemmArgs a = g;
     a.A = lora_a_d;
     a.z_out = z_d;
-    a.split = L.split_d;
     MOELORA_TRY(launch_shrink(a, variant(d, tg, d.inter, true), true, st));
   }
   MOELORA_TRY(mark());
@@ -353,7 +350,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.W = w_down;
     a.B = lora_b_d;
     a.z = z_d;
-    a.n_part = L.part_d;
+    a.waves = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
     MOELORA_TRY(launch_down(a, variant(d, tg, d.inter, lora), st));
   }
   MOELORA_TRY(mark());

@@ -44,31 +44,23 @@ struct GemmArgs {
   const void *W;           // base weights of this projection
   const void *A;           // LoRA A of this projection (shrink kernels)
   const void *B;           // LoRA B of this projection (expand epilogue)
-  const float *z;          // [P][cap][r] shrink partials read by the expand
-  float *z_out;            // [P][cap][r] shrink partials written
-  int n_part;              // P: partials to sum
-  int split;               // workgroup K-splits of the shrink kernels
+  const float *z;          // [cap][r] shrink result read by the expand
+  float *z_out;            // [cap][r] shrink result written
+  int waves;               // waves per workgroup of the GEMM kernels (16 columns each)
   void *h;                 // [cap][I] SiLU(gate)*up, layer dtype
   float *y;                // [R][H] down output per routed row
   AlignBufs al;
 };
 
-// Number of workgroups along the weight-row axis of the GEMM kernels: each
-// covers 64 output columns (4 waves x 16).
-constexpr int kColsPerWg = 64;
-
-// Shrink kernels: partial sums per workgroup split; each of the 4 waves
-// takes one 16-row group of A and one of `ks` K sub-ranges.
-__host__ __device__ inline int shrink_ksub(int r) {
-  int ncg = (r + 15) / 16;
-  return ncg >= 4 ? 1 : 4 / ncg;
-}
+// Shrink kernels: one workgroup of kShrinkWaves waves per LoRA tile.
+constexpr int kShrinkWaves = 16;
 
 // Launchers (return hipGetLastError()).
-hipError_t launch_route(const float *logits, int T, int E, int k, int *ids, float *w,
-                        hipStream_t st);
-hipError_t launch_align(const Shape &s, const int *ids, const int *adapter_ids,
-                        const AlignBufs &al, hipStream_t st);
+// Routing (when logits is non-null; results to ids_ws / w_ws) and the
+// alignment of the routed rows (caller ids when logits is null).
+hipError_t launch_route_align(const Shape &s, const float *logits, const int *ids,
+                              int *ids_ws, float *w_ws, const int *adapter_ids,
+                              const AlignBufs &al, hipStream_t st);
 
 struct GemmVariant {
   bool bf16;     // element type

@@ -139,7 +139,7 @@ def test_stage_timing_hook():
     for _ in range(3):
         run.forward()
     ms, n = L.moelora_timing_end(run.plan.handle)
-    assert n == 3 and all(m >= 0 for m in ms) and ms[3] > 0 and ms[5] > 0
+    assert n == 3 and all(m >= 0 for m in ms) and ms[2] > 0 and ms[4] > 0
 
 
 SAMPLES = {"tiny_fp32": 8, "decode_bf16": 16, "illustrative_bf16": 12,
