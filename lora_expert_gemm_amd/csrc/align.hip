@@ -14,6 +14,9 @@
 // stable ranks, never from the order in which atomics happen to land.
 #include "common.h"
 #include "kernels.h"
+#include "rowlora.h"
+
+#include <type_traits>
 
 namespace moelora {
 
@@ -24,7 +27,6 @@ constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kMaxBuckets = 8448;   // E * (NA + 1)
 constexpr int kMaxAdapterRanks = 256;  // NA + 1
 constexpr int kScatterThreads = 512;
-constexpr int kSmallRows = kAlignThreads / 4;  // fused route + align up to this many rows
 
 __device__ __forceinline__ unsigned long long lanemask_lt(int lane) {
   return (1ull << lane) - 1ull;
@@ -59,16 +61,17 @@ __device__ int block_excl_scan(int v, int *tmp, int *total) {
 // logits.  Lane l holds experts l, l + 64, ...; each of the k rounds takes
 // the wave-wide best untaken (value, index) by a butterfly reduction.  Lanes
 // j < k end with the j-th pick in (*id, *wt).
-constexpr int kRouteMaxPerLane = 1024 / kWave;
-
+// SLOTS = experts per lane (E <= 64 * SLOTS), a template so that small
+// expert counts run a short serial path.
+template <int SLOTS>
 __device__ void route_token(const float *__restrict__ row, int E, int k, int *id, float *wt) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int per = (E + kWave - 1) / kWave;
-  float v[kRouteMaxPerLane];
+  const int per = SLOTS;
+  float v[SLOTS];
 #pragma unroll
-  for (int i = 0; i < kRouteMaxPerLane; ++i) {
+  for (int i = 0; i < SLOTS; ++i) {
     const int e = lane + i * kWave;
-    v[i] = (i < per && e < E) ? row[e] : -__builtin_inff();
+    v[i] = e < E ? row[e] : -__builtin_inff();
   }
   unsigned taken = 0;  // bit i: expert lane + 64 i already chosen
   float my_val = 0.f, top = 0.f;
@@ -77,7 +80,7 @@ __device__ void route_token(const float *__restrict__ row, int E, int k, int *id
     float bv = -__builtin_inff();
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i) {
+    for (int i = 0; i < SLOTS; ++i) {
       const int e = lane + i * kWave;
       if (i < per && e < E && !(taken >> i & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
         bv = v[i];
@@ -109,6 +112,7 @@ __device__ void route_token(const float *__restrict__ row, int E, int k, int *id
 }
 
 // One wave per token.
+template <int SLOTS>
 __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E,
                                                int k, int *__restrict__ ids,
                                                float *__restrict__ w) {
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
   if (t >= T) return;
   int id;
   float wt;
-  route_token(logits + (size_t)t * E, E, k, &id, &wt);
+  route_token<SLOTS>(logits + (size_t)t * E, E, k, &id, &wt);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     w[(size_t)t * k + lane] = wt;
@@ -133,98 +137,101 @@ __device__ __forceinline__ int adapter_rank(const int *aid, int t, int NA, int &
 
 struct AlignSmem {
   int hist[kMaxBuckets];  // rows per (expert, adapter rank) bucket
-  int seg[1024 + 1];      // padded expert starts
   int scan_tmp[kAlignWaves];
 };
 
 // Everything that follows from the bucket histogram (in LDS): padded expert
-// segments, bucket start positions (al.bucket_base / bucket_cnt), padding
-// sentinels, block experts, LoRA segments and their block tiles, the first
-// tile of every block, and the counts.  All 1024 threads call it.
-__device__ void align_layout(const Shape &s, AlignSmem &sm, const AlignBufs &al) {
+// segments, bucket start positions, padding sentinels, block experts, LoRA
+// segments and their block tiles, the first tile of every block, and the
+// counts.  Thread e owns expert e from start to end, so nothing written to
+// global memory is read back, and two block scans place each expert's
+// segments and tiles.
+//
+// Two phases, because a workgroup barrier waits for every global store the
+// workgroup has in flight: align_plan runs the scans (barriers, LDS only)
+// and turns sm.hist[b] into the start position of bucket b; align_store
+// then issues every global store with no barrier after it.
+struct AlignPlan {
+  int seg0, rows, padded;       // owner thread: its expert's segment
+  int seg_off, tile_off;        // owner thread: first LoRA segment / tile
+  int num_padded, n_seg, n_tiles;
+};
+
+__device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
+  const int tid = threadIdx.x;
+  const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM;
+  int *hist = sm.hist;
+  const bool owner = tid < E;  // E <= 1024: one expert per thread
+  AlignPlan P{};
+  int nseg_e = 0, ntile_e = 0;
+  if (owner) {
+    int run = 0;
+    for (int a = 0; a < NR; ++a) {
+      const int c = hist[tid * NR + a];
+      if (a < NA && c > 0) ++nseg_e;
+      run += c;
+    }
+    P.rows = run;
+    P.padded = (run + BM - 1) / BM * BM;
+  }
+  P.seg0 = block_excl_scan(P.padded, sm.scan_tmp, &P.num_padded);
+  if (owner) {  // tiles depend on the absolute start of each bucket
+    int run = P.seg0;
+    for (int a = 0; a < NR; ++a) {
+      const int c = hist[tid * NR + a];
+      if (a < NA && c > 0) ntile_e += (run + c - 1) / BM - run / BM + 1;
+      hist[tid * NR + a] = run;  // bucket start from here on
+      run += c;
+    }
+  }
+  P.seg_off = block_excl_scan(nseg_e, sm.scan_tmp, &P.n_seg);
+  P.tile_off = block_excl_scan(ntile_e, sm.scan_tmp, &P.n_tiles);  // ends with a barrier
+  return P;
+}
+
+__device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan &P,
+                            const AlignBufs &al) {
   const int tid = threadIdx.x;
   const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, R = s.R;
-  int *hist = sm.hist, *seg = sm.seg;
-
-  // padded expert segments (E <= 1024: one expert per thread)
-  int padded = 0;
+  const int *start = sm.hist;
   if (tid < E) {
-    int c = 0;
-    for (int a = 0; a < NR; ++a) c += hist[tid * NR + a];
-    padded = (c + BM - 1) / BM * BM;
-  }
-  int num_padded;
-  const int excl = block_excl_scan(padded, sm.scan_tmp, &num_padded);
-  if (tid < E) seg[tid] = excl;
-  if (tid == 0) seg[E] = num_padded;
-  __syncthreads();
-  for (int i = tid; i <= E; i += kAlignThreads) al.seg_start[i] = seg[i];
-
-  if (tid < E) {
-    int run = seg[tid];
+    const int e = tid, seg0 = P.seg0, seg1 = P.seg0 + P.padded, end = P.seg0 + P.rows;
+    al.seg_start[e] = seg0;
+    int si = P.seg_off, ti = P.tile_off;
+    int b_next = seg0 / BM;  // first block of e whose first tile is not yet written
     for (int a = 0; a < NR; ++a) {
-      const int b = tid * NR + a;
-      al.bucket_base[b] = run;
-      al.bucket_cnt[b] = hist[b];
-      run += hist[b];
+      const int b = e * NR + a, st = start[b];
+      const int c = (a < NA ? start[b + 1] : end) - st;
+      al.bucket_base[b] = st;
+      al.bucket_cnt[b] = c;
+      if (a < NA && c > 0) {
+        reinterpret_cast<int4 *>(al.lora_seg)[si++] = make_int4(e, a, st, c);
+        for (int blk = st / BM; blk <= (st + c - 1) / BM; ++blk) {
+          for (; b_next <= blk; ++b_next) al.block_tile_start[b_next] = ti;
+          const int lo = max(st, blk * BM), hi = min(st + c, (blk + 1) * BM);
+          reinterpret_cast<int4 *>(al.tiles)[ti++] = make_int4(blk, a, lo - blk * BM, hi - lo);
+        }
+      }
     }
-    for (int i = run; i < seg[tid + 1]; ++i) al.sorted_rows[i] = R;
-    for (int b = seg[tid] / BM; b < seg[tid + 1] / BM; ++b) al.block_expert[b] = tid;
+    for (; b_next < seg1 / BM; ++b_next) al.block_tile_start[b_next] = ti;
+    for (int i = end; i < seg1; ++i) al.sorted_rows[i] = R;
+    for (int b = seg0 / BM; b < seg1 / BM; ++b) al.block_expert[b] = e;
   }
-  for (int i = num_padded + tid; i < s.cap; i += kAlignThreads) al.sorted_rows[i] = R;
-  for (int b = num_padded / BM + tid; b < s.nblk; b += kAlignThreads) al.block_expert[b] = -1;
-  __syncthreads();  // bucket_base visible to the whole workgroup
-
-  // LoRA segments (expert, adapter >= 0) and their block tiles: each thread
-  // owns a contiguous range of the E * NA flags.
-  const int nf = E * NA;
-  const int per = (nf + kAlignThreads - 1) / kAlignThreads;
-  const int f0 = min(nf, tid * per), f1 = min(nf, f0 + per);
-  int my_seg = 0, my_tiles = 0;
-  for (int f = f0; f < f1; ++f) {
-    const int b = (f / NA) * NR + f % NA;
-    const int c = hist[b];
-    if (c > 0) {
-      const int st = al.bucket_base[b];
-      ++my_seg;
-      my_tiles += (st + c - 1) / BM - st / BM + 1;
-    }
-  }
-  int n_seg, n_tiles;
-  int seg_i = block_excl_scan(my_seg, sm.scan_tmp, &n_seg);
-  int tile_i = block_excl_scan(my_tiles, sm.scan_tmp, &n_tiles);
-  for (int f = f0; f < f1; ++f) {
-    const int e = f / NA, a = f % NA, b = e * NR + a;
-    const int c = hist[b];
-    if (c <= 0) continue;
-    const int st = al.bucket_base[b], en = st + c;
-    reinterpret_cast<int4 *>(al.lora_seg)[seg_i++] = make_int4(e, a, st, c);
-    for (int blk = st / BM; blk <= (en - 1) / BM; ++blk) {
-      const int lo = max(st, blk * BM), hi = min(en, (blk + 1) * BM);
-      reinterpret_cast<int4 *>(al.tiles)[tile_i++] = make_int4(blk, a, lo - blk * BM, hi - lo);
-    }
-  }
-  for (int i = n_seg + tid; i < s.max_seg; i += kAlignThreads)
-    reinterpret_cast<int4 *>(al.lora_seg)[i] = make_int4(-1, -1, 0, 0);
-  for (int i = n_tiles + tid; i < s.max_tiles; i += kAlignThreads)
-    reinterpret_cast<int4 *>(al.tiles)[i] = make_int4(-1, -1, 0, 0);
-  __syncthreads();  // tiles visible
-
-  for (int i = tid; i < n_tiles; i += kAlignThreads) {
-    const int bi = al.tiles[4 * i];
-    const int bp = i ? al.tiles[4 * (i - 1)] : -1;
-    for (int b = bp + 1; b <= bi; ++b) al.block_tile_start[b] = i;
-  }
-  {
-    const int last = n_tiles ? al.tiles[4 * (n_tiles - 1)] : -1;
-    for (int b = last + 1 + tid; b <= s.nblk; b += kAlignThreads) al.block_tile_start[b] = n_tiles;
-  }
+  const int np = P.num_padded;
   if (tid == 0) {
-    al.counts[0] = num_padded;
-    al.counts[1] = n_seg;
-    al.counts[2] = n_tiles;
+    al.seg_start[E] = np;
+    al.counts[0] = np;
+    al.counts[1] = P.n_seg;
+    al.counts[2] = P.n_tiles;
     al.counts[3] = 0;
   }
+  for (int i = np + tid; i < s.cap; i += kAlignThreads) al.sorted_rows[i] = R;
+  for (int b = np / BM + tid; b < s.nblk; b += kAlignThreads) al.block_expert[b] = -1;
+  for (int b = np / BM + tid; b <= s.nblk; b += kAlignThreads) al.block_tile_start[b] = P.n_tiles;
+  for (int i = P.n_seg + tid; i < s.max_seg; i += kAlignThreads)
+    reinterpret_cast<int4 *>(al.lora_seg)[i] = make_int4(-1, -1, 0, 0);
+  for (int i = P.n_tiles + tid; i < s.max_tiles; i += kAlignThreads)
+    reinterpret_cast<int4 *>(al.tiles)[i] = make_int4(-1, -1, 0, 0);
 }
 
 // Alignment metadata for any batch, one workgroup: bucket histogram, then
@@ -237,6 +244,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
   __shared__ int tok_base[kMaxAdapterRanks];
   __shared__ int cursor[kMaxAdapterRanks];
   __shared__ int wtab[kAlignWaves][kMaxAdapterRanks];
+  __shared__ int err_all;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int E = s.E, NA = s.NA, NR = NA + 1, R = s.R, k = s.k, T = s.T;
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
     cursor[i] = 0;
   }
   for (int i = tid; i < kAlignWaves * NR; i += kAlignThreads) wtab[i / NR][i % NR] = 0;
-  if (tid == 0) *al.error = 0;
+  if (tid == 0) err_all = 0;
   __syncthreads();
 
   int err = 0;
@@ -262,19 +270,16 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
     int dummy = 0;
     atomicAdd(&sm.hist[e * NR + adapter_rank(aid, p / k, NA, dummy)], 1);
   }
-  if (err) atomicOr(al.error, err);
+  if (err) atomicOr(&err_all, err);
   __syncthreads();
 
-  align_layout(s, sm, al);
-
+  const AlignPlan P = align_plan(s, sm);
   if (tid == 0) {
     int run = 0;
     for (int a = 0; a < NR; ++a) {
       tok_base[a] = run;
-      al.tok_off[a] = run;
       run += tok_cnt[a];
     }
-    al.tok_off[NR] = run;
   }
   __syncthreads();
 
@@ -311,6 +316,10 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
     }
     __syncthreads();
   }
+
+  align_store(s, sm, P, al);
+  for (int a = tid; a <= NR; a += kAlignThreads) al.tok_off[a] = a < NR ? tok_base[a] : T;
+  if (tid == 0) *al.error = err_all;
 }
 
 // Alignment scatter: one workgroup per (expert, adapter rank) bucket writes
@@ -355,16 +364,62 @@ __global__ __launch_bounds__(kScatterThreads) void k_align_scatter(Shape s,
   }
 }
 
+// Gate_up shrink of routed row p = blockIdx.x - 1, riding along with the
+// routing + alignment workgroup: the workgroup routes its own token (the
+// same deterministic routing as workgroup 0), then computes
+// z[p] = x[t] . A_gu[a_t][e_p]^T with the whole workgroup.
+template <int SLOTS, typename DT>
+__device__ void route_row_shrink(const Shape &s, const float *__restrict__ logits,
+                                 const int *__restrict__ ids_in, const RowShrinkArgs &rs,
+                                 float *red) {
+  __shared__ int s_e;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int p = blockIdx.x - 1, t = p / s.k, j = p % s.k;
+  const int a = rs.adapter_ids[t];
+  if (a < 0 || a >= s.NA) return;  // no adapter: nothing to shrink
+  if (tid < kWave) {
+    int e = -1;
+    if (logits) {
+      int id;
+      float wt;
+      route_token<SLOTS>(logits + (size_t)t * s.E, s.E, s.k, &id, &wt);
+      e = __shfl(id, j);
+    } else {
+      e = ids_in[p];
+    }
+    if (lane == 0) s_e = e;
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e < 0 || e >= s.E) return;
+  const DT *x = static_cast<const DT *>(rs.x) + (size_t)t * rs.K;
+  const DT *A = static_cast<const DT *>(rs.A) + ((size_t)a * s.E + e) * s.r * rs.K;
+  if (rs.vec)
+    row_shrink<DT, true>(x, A, rs.K, s.r, rs.z + (size_t)p * s.r, red);
+  else
+    row_shrink<DT, false>(x, A, rs.K, s.r, rs.z + (size_t)p * s.r, red);
+}
+
 // Small batches (R <= kSmallRows routed rows): routing and the whole
-// alignment in one workgroup.  Rows are ranked inside their bucket by
+// alignment in workgroup 0.  Rows are ranked inside their bucket by
 // counting the earlier rows with the same key (R comparisons from LDS per
-// row), which yields the same stable order as the two-kernel path.
+// row), which yields the same stable order as the two-kernel path.  With
+// a row shrink (DT not void), workgroups 1..R shrink one routed row each.
+template <int SLOTS, typename DT>
 __global__ __launch_bounds__(kAlignThreads) void k_route_align_small(
     Shape s, const float *__restrict__ logits, const int *__restrict__ ids_in,
     int *__restrict__ ids_out, float *__restrict__ w_out, const int *__restrict__ aid,
-    AlignBufs al) {
+    AlignBufs al, RowShrinkArgs rs) {
   __shared__ AlignSmem sm;
   __shared__ int key[kSmallRows];
+  __shared__ float wts[kSmallRows];
+  __shared__ int err_all;
+  if constexpr (!std::is_void_v<DT>) {
+    if (blockIdx.x > 0) {
+      route_row_shrink<SLOTS, DT>(s, logits, ids_in, rs, reinterpret_cast<float *>(sm.hist));
+      return;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int E = s.E, NA = s.NA, NR = NA + 1, R = s.R, k = s.k, T = s.T;
   const int NB = E * NR;
@@ -373,59 +428,80 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align_small(
     for (int t = wv; t < T; t += kAlignWaves) {
       int id;
       float wt;
-      route_token(logits + (size_t)t * E, E, k, &id, &wt);
+      route_token<SLOTS>(logits + (size_t)t * E, E, k, &id, &wt);
       if (lane < k) {
-        ids_out[t * k + lane] = id;
-        w_out[t * k + lane] = wt;
         key[t * k + lane] = id;
+        wts[t * k + lane] = wt;
       }
     }
   } else {
     for (int p = tid; p < R; p += kAlignThreads) key[p] = ids_in[p];
   }
   for (int i = tid; i < NB; i += kAlignThreads) sm.hist[i] = 0;
-  if (tid == 0) *al.error = 0;
+  if (tid == 0) err_all = 0;
   __syncthreads();
 
   // key = expert * (NA + 1) + adapter rank, or -1 for a dropped row
-  int err = 0;
-  int my_key = -1;
+  int err = 0, my_key = -1, my_id = 0;
   if (tid < R) {
-    const int e = key[tid];
+    my_id = key[tid];
     const int ar = adapter_rank(aid, tid / k, NA, err);
-    if (e < 0 || e >= E) {
+    if (my_id < 0 || my_id >= E) {
       err |= MOELORA_DEVERR_EXPERT_ID;
     } else {
-      my_key = e * NR + ar;
+      my_key = my_id * NR + ar;
       atomicAdd(&sm.hist[my_key], 1);
     }
   }
-  if (err) atomicOr(al.error, err);
+  if (err) atomicOr(&err_all, err);
   __syncthreads();
   if (tid < R) key[tid] = my_key;
 
-  align_layout(s, sm, al);  // contains barriers: key[] is visible after it
+  const AlignPlan P = align_plan(s, sm);  // ends with a barrier: key[] visible
 
+  // stable rank inside the bucket: earlier rows with the same key
   if (my_key >= 0) {
     int rank = 0;
+#pragma unroll 8
     for (int q = 0; q < tid; ++q) rank += key[q] == my_key;
-    al.sorted_rows[al.bucket_base[my_key] + rank] = tid;
+    al.sorted_rows[sm.hist[my_key] + rank] = tid;  // hist holds bucket starts
+    al.row_pos[tid] = sm.hist[my_key] + rank;
   }
+  if (logits && tid < R) {
+    ids_out[tid] = my_id;
+    w_out[tid] = wts[tid];
+  }
+  align_store(s, sm, P, al);
+  if (tid == 0) *al.error = err_all;
 }
 
-}  // namespace
+template <int SLOTS, typename DT>
+hipError_t launch_small(const Shape &s, const float *logits, const int *ids, int *ids_ws,
+                        float *w_ws, const int *adapter_ids, const AlignBufs &al,
+                        const RowShrinkArgs &rs, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_route_align_small<SLOTS, DT>), dim3(grid), dim3(kAlignThreads), 0, st, s,
+                     logits, ids, ids_ws, w_ws, adapter_ids, al, rs);
+  return hipGetLastError();
+}
 
-hipError_t launch_route_align(const Shape &s, const float *logits, const int *ids,
-                              int *ids_ws, float *w_ws, const int *adapter_ids,
-                              const AlignBufs &al, hipStream_t st) {
+template <int SLOTS>
+hipError_t launch_route_align_t(const Shape &s, const float *logits, const int *ids, int *ids_ws,
+                                float *w_ws, const int *adapter_ids, const AlignBufs &al,
+                                const RowShrinkArgs *rs, bool bf16, hipStream_t st) {
   if (s.R <= kSmallRows) {
-    hipLaunchKernelGGL(k_route_align_small, dim3(1), dim3(kAlignThreads), 0, st, s, logits, ids,
-                       ids_ws, w_ws, adapter_ids, al);
-    return hipGetLastError();
+    if (!rs)
+      return launch_small<SLOTS, void>(s, logits, ids, ids_ws, w_ws, adapter_ids, al,
+                                       RowShrinkArgs{}, 1, st);
+    if (bf16)
+      return launch_small<SLOTS, uint16_t>(s, logits, ids, ids_ws, w_ws, adapter_ids, al, *rs,
+                                           1 + s.R, st);
+    return launch_small<SLOTS, float>(s, logits, ids, ids_ws, w_ws, adapter_ids, al, *rs,
+                                      1 + s.R, st);
   }
+  if (rs) return hipErrorInvalidValue;  // row shrinks ride along with small batches only
   if (logits) {
-    hipLaunchKernelGGL(k_route, dim3((s.T + 3) / 4), dim3(256), 0, st, logits, s.T, s.E, s.k,
-                       ids_ws, w_ws);
+    hipLaunchKernelGGL(k_route<SLOTS>, dim3((s.T + 3) / 4), dim3(256), 0, st, logits, s.T, s.E,
+                       s.k, ids_ws, w_ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ids = ids_ws;
@@ -436,6 +512,21 @@ hipError_t launch_route_align(const Shape &s, const float *logits, const int *id
   hipLaunchKernelGGL(k_align_scatter, dim3(s.E * (s.NA + 1)), dim3(kScatterThreads), 0, st, s,
                      ids, al);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route_align(const Shape &s, const float *logits, const int *ids,
+                              int *ids_ws, float *w_ws, const int *adapter_ids,
+                              const AlignBufs &al, const RowShrinkArgs *rs, bool bf16,
+                              hipStream_t st) {
+#define MOELORA_RA(SL) \
+  launch_route_align_t<SL>(s, logits, ids, ids_ws, w_ws, adapter_ids, al, rs, bf16, st)
+  if (s.E <= 64) return MOELORA_RA(1);
+  if (s.E <= 128) return MOELORA_RA(2);
+  if (s.E <= 256) return MOELORA_RA(4);
+  return MOELORA_RA(16);
+#undef MOELORA_RA
 }
 
 }  // namespace moelora

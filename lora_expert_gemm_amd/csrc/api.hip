@@ -58,12 +58,19 @@ int choose_waves(int tg, bool gate_up) {
   return 4;
 }
 
+// Workgroups sharing one shrink tile's contraction: a decode step has only
+// tens of LoRA tiles, so each is split over several CUs.
+int choose_split(int tg, int R) {
+  if (tg != kTgSmall) return 1;
+  return std::max(1, std::min(8, 512 / std::max(R, 1)));
+}
+
 struct Layout {
   Shape s;
-  int waves_gu, waves_d;
+  int waves_gu, waves_d, split;
   size_t off_error, off_counts, off_ids, off_w, off_sorted, off_bexp, off_seg, off_lseg,
-      off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_zgu, off_zd, off_h,
-      off_y, total;
+      off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_rpos, off_zgu, off_zd,
+      off_h, off_y, total;
 };
 
 Layout make_layout(const moelora_desc &d, int T) {
@@ -87,6 +94,7 @@ Layout make_layout(const moelora_desc &d, int T) {
   const int tg = s.BM / 16;
   L.waves_gu = choose_waves(tg, true);
   L.waves_d = choose_waves(tg, false);
+  L.split = choose_split(tg, s.R);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
   const size_t NB = (size_t)s.E * (s.NA + 1);
   size_t o = 0;
@@ -109,8 +117,10 @@ Layout make_layout(const moelora_desc &d, int T) {
   L.off_bbase = take(4 * NB);
   L.off_tperm = take(4ull * T);
   L.off_toff = take(4ull * (s.NA + 2));
-  L.off_zgu = take(4ull * s.cap * s.r);
-  L.off_zd = take(4ull * s.cap * s.r);
+  L.off_rpos = take(4ull * s.R);
+  // z: tile-wise [split][cap][r] partial sums, or row-wise [R][r] (R <= cap)
+  L.off_zgu = take(4ull * L.split * s.cap * s.r);
+  L.off_zd = take(4ull * L.split * s.cap * s.r);
   L.off_h = take(es * s.cap * s.I);
   L.off_y = take(4ull * s.R * s.H);
   L.total = o;
@@ -136,7 +146,7 @@ moelora_status check_desc(const moelora_desc *d) {
   return MOELORA_OK;
 }
 
-GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora) {
+GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora, bool rowz = false) {
   GemmVariant v;
   v.bf16 = d.dtype == MOELORA_BF16;
   const int epc = v.bf16 ? 8 : 4;
@@ -145,7 +155,19 @@ GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora) {
   v.vec = d.hidden % epc == 0 && d.inter % epc == 0 && (d.rank == 0 || d.rank % epc == 0);
   v.even_k = v.vec && K % ks == 0;
   v.lora = lora;
+  v.rowz = rowz;
   return v;
+}
+
+// Row-wise LoRA (decode-sized batches): the shrinks ride along with the
+// routing/alignment launch and the down launch, and the down expand moves
+// into the combine.  Needs the one-workgroup alignment and down workgroups
+// with at least r (rounded up to a power of two) threads.
+bool use_row_mode(const Shape &s, bool lora, int waves_d) {
+  if (!lora || s.R > kSmallRows || s.BM != 16) return false;
+  int rp = 1;
+  while (rp < s.r) rp <<= 1;
+  return 64 * waves_d >= rp;  // 64 threads per wave
 }
 
 int k_tail(const moelora_desc &d, int K) {
@@ -240,9 +262,12 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   const int wd = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
   snprintf(buf, buf_len,
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
-           "k_tail_d=%d waves_gu=%d waves_d=%d shrink_waves=%d cap=%d workspace=%zu",
+           "k_tail_d=%d waves_gu=%d waves_d=%d lora_mode=%s shrink_split=%d cap=%d "
+           "workspace=%zu",
            vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
-           k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, kShrinkWaves, L.s.cap, L.total);
+           k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd,
+           d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile", L.split,
+           L.s.cap, L.total);
   return MOELORA_OK;
 }
 
@@ -290,6 +315,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   al.bucket_base = reinterpret_cast<int *>(ws + L.off_bbase);
   al.tok_perm = reinterpret_cast<int *>(ws + L.off_tperm);
   al.tok_off = reinterpret_cast<int *>(ws + L.off_toff);
+  al.row_pos = reinterpret_cast<int *>(ws + L.off_rpos);
 
   hipEvent_t *ev = nullptr;
   if (plan->timing && plan->n_calls < plan->max_calls)
@@ -303,26 +329,36 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     if ((expr) != hipSuccess) return MOELORA_ERR_HIP; \
   } while (0)
 
+  const int waves_gu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
+  const int waves_d = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
+  const bool row = use_row_mode(s, lora, waves_d);
+  const GemmVariant vg = variant(d, tg, d.hidden, lora, row);
+  const GemmVariant vd = variant(d, tg, d.inter, lora, row);
+  float *z_gu = reinterpret_cast<float *>(ws + L.off_zgu);
+  float *z_d = reinterpret_cast<float *>(ws + L.off_zd);
+  void *h = ws + L.off_h;
+
   MOELORA_TRY(mark());
   int *ids_ws = reinterpret_cast<int *>(ws + L.off_ids);
   float *w_ws = reinterpret_cast<float *>(ws + L.off_w);
+  RowShrinkArgs rs_gu{x, lora_a_gu, z_gu, adapter_ids, d.hidden, vg.vec};
   MOELORA_TRY(launch_route_align(s, own_route ? router_logits : nullptr, topk_ids, ids_ws, w_ws,
-                                 lora ? adapter_ids : nullptr, al, st));
+                                 lora ? adapter_ids : nullptr, al, row ? &rs_gu : nullptr,
+                                 vg.bf16, st));
   const int *ids = own_route ? ids_ws : topk_ids;
   const float *wts = own_route ? w_ws : topk_w;
   MOELORA_TRY(mark());
 
   GemmArgs g{};
   g.s = s;
+  g.split = L.split;
   g.topk_ids = ids;
   g.x = x;
   g.al = al;
-  g.h = ws + L.off_h;
+  g.h = h;
   g.y = reinterpret_cast<float *>(ws + L.off_y);
-  float *z_gu = reinterpret_cast<float *>(ws + L.off_zgu);
-  float *z_d = reinterpret_cast<float *>(ws + L.off_zd);
 
-  if (lora) {
+  if (lora && !row) {
     GemmArgs a = g;
     a.A = lora_a_gu;
     a.z_out = z_gu;
@@ -334,11 +370,11 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.W = w_gate_up;
     a.B = lora_b_gu;
     a.z = z_gu;
-    a.waves = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
-    MOELORA_TRY(launch_gate_up(a, variant(d, tg, d.hidden, lora), st));
+    a.waves = waves_gu;
+    MOELORA_TRY(launch_gate_up(a, vg, st));
   }
   MOELORA_TRY(mark());
-  if (lora) {
+  if (lora && !row) {
     GemmArgs a = g;
     a.A = lora_a_d;
     a.z_out = z_d;
@@ -350,11 +386,16 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.W = w_down;
     a.B = lora_b_d;
     a.z = z_d;
-    a.waves = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
-    MOELORA_TRY(launch_down(a, variant(d, tg, d.inter, lora), st));
+    a.waves = waves_d;
+    if (row) {
+      a.rs = RowShrinkArgs{h, lora_a_d, z_d, adapter_ids, d.inter, vd.vec};
+      a.row_wgs = s.R;
+    }
+    MOELORA_TRY(launch_down(a, vd, st));
   }
   MOELORA_TRY(mark());
-  MOELORA_TRY(launch_combine(s, ids, wts, g.y, out, d.dtype == MOELORA_BF16, st));
+  MOELORA_TRY(launch_combine(s, ids, wts, g.y, out, d.dtype == MOELORA_BF16, row ? z_d : nullptr,
+                             lora_b_d, adapter_ids, vd.vec, st));
   MOELORA_TRY(mark());
 #undef MOELORA_TRY
   return MOELORA_OK;

@@ -40,6 +40,15 @@ template <> struct Elem<float> {
   __device__ static float from_f32(float v) { return v; }
 };
 
+// The elements of a chunk, as a value (no address taken).
+template <typename DT> struct Chunk {
+  DT v[Elem<DT>::kPerChunk];
+};
+template <typename DT>
+__device__ __forceinline__ Chunk<DT> chunk_elems(u32x4_t c) {
+  return __builtin_bit_cast(Chunk<DT>, c);
+}
+
 // One contraction step of a 16x16 output tile:  D[i][j] += sum_k A[i][k] B[k][j]
 // where the lane l supplies row i = l % 16 of A and column j = l % 16 of B,
 // both as one chunk covering the same contraction indices.  bf16: one

@@ -30,6 +30,7 @@
 // fixed order, so results never depend on scheduling.
 #include "common.h"
 #include "kernels.h"
+#include "rowlora.h"
 
 namespace moelora {
 
@@ -99,10 +100,10 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
 // The expand of one projection, added into the base accumulators:
 // acc[tg] += B_rows . z^T for the block's LoRA tiles.  z (float) feeds the
 // MFMA as a bf16 hi + lo pair (a split exact to about 2^-16) or as float.
-template <typename DT, int TG, bool VEC, bool TWO>
+template <typename DT, int TG, bool VEC, bool TWO, bool ROWZ>
 __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, const DT *Bbase,
                                        size_t b_rows, int row, size_t row_off1, int kg, int ri,
-                                       f32x4_t *acc0, f32x4_t *acc1) {
+                                       const int *prow, f32x4_t *acc0, f32x4_t *acc1) {
   using M = Mma<DT>;
   constexpr int EPC = Elem<DT>::kPerChunk;
   constexpr int KS = M::kK;
@@ -126,22 +127,30 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, const 
 #pragma unroll
         for (int q = 0; q < EPC; ++q) zv[q] = 0.f;
         if (local >= lo && local < lo + n) {
-          const float *zp = a.z + ((size_t)blk * BM + local) * r + kk;
+          // z = sum of the shrink's split partials, in split order (row
+          // mode: one final z per routed row)
+          const float *zp = ROWZ ? a.z + (size_t)prow[tg] * r + kk
+                                 : a.z + ((size_t)blk * BM + local) * r + kk;
+          const size_t stride = (size_t)s.cap * r;
+          const int nsplit = ROWZ ? 1 : a.split;
           if (VEC) {  // r is a multiple of the chunk: whole chunk in or out
             if (kk < r) {
+              for (int sp = 0; sp < nsplit; ++sp) {
 #pragma unroll
-              for (int q = 0; q < EPC; q += 4) {
-                const float4 v4 = *reinterpret_cast<const float4 *>(zp + q);
-                zv[q] = v4.x;
-                zv[q + 1] = v4.y;
-                zv[q + 2] = v4.z;
-                zv[q + 3] = v4.w;
+                for (int q = 0; q < EPC; q += 4) {
+                  const float4 v4 = *reinterpret_cast<const float4 *>(zp + sp * stride + q);
+                  zv[q] += v4.x;
+                  zv[q + 1] += v4.y;
+                  zv[q + 2] += v4.z;
+                  zv[q + 3] += v4.w;
+                }
               }
             }
           } else {
+            for (int sp = 0; sp < nsplit; ++sp)
 #pragma unroll
-            for (int q = 0; q < EPC; ++q)
-              if (kk + q < r) zv[q] = zp[q];
+              for (int q = 0; q < EPC; ++q)
+                if (kk + q < r) zv[q] += zp[sp * stride + q];
           }
         }
         u32x4_t zh, zl;
@@ -162,8 +171,8 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, const 
 struct GemmTile {
   int blk, nt;
 };
-__device__ __forceinline__ GemmTile gemm_tile(int nblk) {
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+__device__ __forceinline__ GemmTile gemm_tile(int nblk, int bid, int nb) {
+  const int L = xcd_remap(bid, nb);
   return {L % nblk, L / nblk};
 }
 
@@ -171,13 +180,15 @@ __device__ __forceinline__ GemmTile gemm_tile(int nblk) {
 // sorted rows; a wave's 16 h-columns n need weight rows n (gate) and I + n
 // (up), so SiLU * up is formed in registers.  h is written for the block's
 // real rows (padding rows are skipped by every reader).
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, bool LORA>
+// MODE: 0 no LoRA, 1 tile-wise (z per sorted position, split partials),
+// 2 row-wise (z per routed row).
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE>
 __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int ri = lane & 15, kg = lane >> 4;
-  const GemmTile gt = gemm_tile(s.nblk);
+  const GemmTile gt = gemm_tile(s.nblk, blockIdx.x, gridDim.x);
   const int blk = gt.blk;
   const int e = a.al.block_expert[blk];  // -1 past the padded rows
   const int I = s.I, H = s.H;
@@ -188,10 +199,12 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   const DT *wu = wg + (size_t)I * H;
   const DT *xr[TG];
   bool ok[TG];
+  int prow[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     const int p = a.al.sorted_rows[blk * BM + tg * 16 + ri];
     ok[tg] = p < s.R;
+    prow[tg] = p;
     xr[tg] = static_cast<const DT *>(a.x) + (size_t)(ok[tg] ? p / s.k : 0) * H;
   }
   f32x4_t ag[TG], au[TG];
@@ -201,9 +214,9 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
     au[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, ok, H, kg, ag, au);
-  if (LORA)
-    expand<DT, TG, VEC, true>(a, blk, e, static_cast<const DT *>(a.B), (size_t)2 * I, nrow,
-                              (size_t)I, kg, ri, ag, au);
+  if (MODE != 0)
+    expand<DT, TG, VEC, true, MODE == 2>(a, blk, e, static_cast<const DT *>(a.B), (size_t)2 * I,
+                                         nrow, (size_t)I, kg, ri, prow, ag, au);
   DT *hout = static_cast<DT *>(a.h);
   const int nb = n0 + kg * 4;
 #pragma unroll
@@ -227,14 +240,33 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   }
 }
 
-// down GEMM + expand, written per routed row: y[p][m] (float).
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, bool LORA>
+// down GEMM (+ expand when MODE == 1), written per routed row: y[p][m]
+// (float).  MODE 2 (row-wise LoRA): the first a.row_wgs workgroups compute
+// the down shrink of one routed row each, z_d[p] = h[pos_p] . A_d[a][e]^T,
+// alongside the base GEMM (both only need h); the expand then happens in
+// the combine.
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE>
 __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
+  int bid = blockIdx.x, nb = gridDim.x;
+  if constexpr (MODE == 2) {
+    __shared__ float red[256];
+    if (bid < a.row_wgs) {
+      const int p = bid, t = p / s.k;
+      const int ad = a.rs.adapter_ids[t], e = a.topk_ids[p];
+      if (ad < 0 || ad >= s.NA || e < 0 || e >= s.E) return;
+      const DT *h = static_cast<const DT *>(a.rs.x) + (size_t)a.al.row_pos[p] * s.I;
+      const DT *A = static_cast<const DT *>(a.rs.A) + ((size_t)ad * s.E + e) * s.r * s.I;
+      row_shrink<DT, VEC>(h, A, s.I, s.r, a.rs.z + (size_t)p * s.r, red);
+      return;
+    }
+    bid -= a.row_wgs;
+    nb -= a.row_wgs;
+  }
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int ri = lane & 15, kg = lane >> 4;
-  const GemmTile gt = gemm_tile(s.nblk);
+  const GemmTile gt = gemm_tile(s.nblk, bid, nb);
   const int blk = gt.blk;
   const int e = a.al.block_expert[blk];
   const int I = s.I, H = s.H;
@@ -255,9 +287,9 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   contract<DT, TG, U, VEC, EVEN_K, false>(wd, wd, xr, ok, I, kg, acc, acc);
-  if (LORA)
-    expand<DT, TG, VEC, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow, 0, kg,
-                               ri, acc, acc);
+  if (MODE == 1)
+    expand<DT, TG, VEC, false, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow, 0,
+                                      kg, ri, prow, acc, acc);
   const int mb = m0 + kg * 4;
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
@@ -274,12 +306,15 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
 }
 
 // LoRA shrink z = X A^T for the rows of one LoRA tile; X is x (gate_up,
-// rows by token) or h (down, rows by sorted position).  One workgroup per
-// tile.  Wave tasks are (16-row group of A, token group, contraction part);
-// when there are fewer (row group, token group) pairs than waves, the
-// contraction is split into nks parts whose partial sums go to LDS and are
-// added in part order (split-K across waves; the partials are reduced by a
-// second pass inside the workgroup rather than by atomics).
+// rows by token) or h (down, rows by sorted position).  Workgroup (tile,
+// split) takes one split of the contraction (split-K across workgroups, so
+// the skinny shrink of a decode step spreads over many CUs).  Inside it,
+// wave tasks are (16-row group of A, token group, contraction part); when
+// there are fewer (row group, token group) pairs than waves the split is cut
+// again, those partial sums meet in LDS and are added in part order.  The
+// result of split s goes to z_out[s][pos][c]; the expand that consumes z
+// adds the splits in split order: no atomics, no scheduling-dependent
+// rounding.
 template <typename DT, int TG, bool VEC, bool EVEN_K, bool FROM_H>
 __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
   using M = Mma<DT>;
@@ -290,7 +325,7 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
   // kShrinkWaves * 16 * 16 floats (r <= 16 * ncg and nks * ncg * ntg <= waves)
   __shared__ float part[kShrinkWaves * 16 * 16];
   const Shape &s = a.s;
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x, split = blockIdx.y;
   if (tile >= a.al.counts[2]) return;
   const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[tile];
   const int blk = tl.x, ad = tl.y, lo = tl.z, n = tl.w;
@@ -303,12 +338,16 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
   const int tg_lo = lo / 16, tg_hi = (lo + n - 1) / 16, ntg = tg_hi - tg_lo + 1;
   const int pairs = ncg * ntg;
   const int nks = pairs >= kShrinkWaves ? 1 : kShrinkWaves / pairs;
-  const int nsteps = (K + KS - 1) / KS;
+  const int nsteps_all = (K + KS - 1) / KS;
+  const int split_beg = (int)((long long)split * nsteps_all / a.split);
+  const int split_end = (int)((long long)(split + 1) * nsteps_all / a.split);
+  const int nsteps = split_end - split_beg;
+  float *dst = a.z_out + (size_t)split * s.cap * r;
 
   for (int u = wave; u < pairs * nks; u += kShrinkWaves) {
     const int cg = u % ncg, tg = tg_lo + (u / ncg) % ntg, ks = u / pairs;
-    const int s_beg = (int)((long long)ks * nsteps / nks);
-    const int s_end = (int)((long long)(ks + 1) * nsteps / nks);
+    const int s_beg = split_beg + (int)((long long)ks * nsteps / nks);
+    const int s_end = split_beg + (int)((long long)(ks + 1) * nsteps / nks);
     const int crow = min(cg * 16 + ri, r - 1);
     const DT *arow = static_cast<const DT *>(a.A) + (((size_t)ad * s.E + e) * r + crow) * K;
     const int local = tg * 16 + ri;
@@ -330,7 +369,7 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
         const int st = st0 + u;
         const int k = st * KS + kg * EPC;
         const bool live = st < s_end;
-        const bool tail = !EVEN_K && st == nsteps - 1;
+        const bool tail = !EVEN_K && st == nsteps_all - 1;
         av[u] = u32x4_t{0, 0, 0, 0};
         bv[u] = u32x4_t{0, 0, 0, 0};
         if (live) av[u] = tail ? load_chunk_any<DT, VEC>(arow, k, K) : ld<DT, VEC>(arow, k, K);
@@ -345,7 +384,7 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
       const int c = cg * 16 + kg * 4 + v;
       if (c >= r) continue;
       if (nks == 1) {
-        if (in) a.z_out[pos * r + c] = acc[v];
+        if (in) dst[pos * r + c] = acc[v];
       } else {
         part[(ks * 16 * ntg + (tg - tg_lo) * 16 + ri) * r + c] = acc[v];
       }
@@ -359,42 +398,88 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
     if (local < lo || local >= lo + n) continue;
     float sum = 0.f;
     for (int ks = 0; ks < nks; ++ks) sum += part[(ks * 16 * ntg + row) * r + c];
-    a.z_out[((size_t)blk * BM + local) * r + c] = sum;
+    dst[((size_t)blk * BM + local) * r + c] = sum;
   }
 }
 
 // out[t] = sum_j w[t][j] * y[t*k + j] in ascending j (float), rounded to
-// the layer dtype; rows with an out-of-range expert id add nothing.
-template <typename DT>
+// the layer dtype; rows with an out-of-range expert id add nothing.  With
+// z_d (row-wise LoRA), each row first gets its down expand added:
+// y[p][m] += sum_c z_d[p][c] B_d[a][e][m][c] (the expand is linear, so it
+// may follow the base GEMM in a later kernel).
+template <typename DT, bool VEC>
 __global__ __launch_bounds__(256) void k_combine(Shape s, const int *__restrict__ ids,
                                                  const float *__restrict__ w,
-                                                 const float *__restrict__ y, DT *out) {
+                                                 const float *__restrict__ y, DT *out,
+                                                 const float *__restrict__ z_d,
+                                                 const DT *__restrict__ B_d,
+                                                 const int *__restrict__ aid) {
   const int t = blockIdx.x;
-  const int m = (blockIdx.y * 256 + threadIdx.x) * 4;
+  const int m0 = (blockIdx.y * 256 + threadIdx.x) * 4;
   const int H = s.H;
-  if (m >= H) return;
+  if (m0 >= H) return;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool vec = (H % 4) == 0;
   for (int j = 0; j < s.k; ++j) {
     const int p = t * s.k + j;
     const int e = ids[p];
     if (e < 0 || e >= s.E) continue;
     const float wj = w[p];
-    const float *yr = y + (size_t)p * H + m;
-    if (vec) {
-      const float4 v = *reinterpret_cast<const float4 *>(yr);
-      acc[0] += wj * v.x;
-      acc[1] += wj * v.y;
-      acc[2] += wj * v.z;
-      acc[3] += wj * v.w;
+    const float *yr = y + (size_t)p * H + m0;
+    if (VEC) {
+      const float4 v4 = *reinterpret_cast<const float4 *>(yr);
+      acc[0] += wj * v4.x;
+      acc[1] += wj * v4.y;
+      acc[2] += wj * v4.z;
+      acc[3] += wj * v4.w;
     } else {
       for (int q = 0; q < 4; ++q)
-        if (m + q < H) acc[q] += wj * yr[q];
+        if (m0 + q < H) acc[q] += wj * yr[q];
     }
   }
-  DT *o = out + (size_t)t * H + m;
+  DT *o = out + (size_t)t * H + m0;
   for (int q = 0; q < 4; ++q)
-    if (m + q < H) o[q] = Elem<DT>::from_f32(acc[q]);
+    if (m0 + q < H) o[q] = Elem<DT>::from_f32(acc[q]);
+}
+
+// Row-wise LoRA variant: one thread per output column m, and each routed
+// row first gets its down expand, y[p][m] += sum_c z_d[p][c] B_d[a][e][m][c]
+// (linear, so it may follow the base GEMM in a later kernel).  A wave's 64
+// threads read 64 consecutive rows of B_d, i.e. one contiguous run.
+template <typename DT, bool VEC>
+__global__ __launch_bounds__(64) void k_combine_rows(Shape s, const int *__restrict__ ids,
+                                                     const float *__restrict__ w,
+                                                     const float *__restrict__ y, DT *out,
+                                                     const float *__restrict__ z_d,
+                                                     const DT *__restrict__ B_d,
+                                                     const int *__restrict__ aid) {
+  constexpr int EPC = Elem<DT>::kPerChunk;
+  const int t = blockIdx.x;
+  const int m = blockIdx.y * 64 + threadIdx.x;
+  const int H = s.H, r = s.r;
+  if (m >= H) return;
+  int ad = aid[t];
+  if (ad < 0 || ad >= s.NA) ad = -1;
+  float acc = 0.f;
+  for (int j = 0; j < s.k; ++j) {
+    const int p = t * s.k + j;
+    const int e = ids[p];
+    if (e < 0 || e >= s.E) continue;
+    float v = y[(size_t)p * H + m];
+    if (ad >= 0) {
+      const float *zp = z_d + (size_t)p * r;
+      const DT *b = B_d + (((size_t)ad * s.E + e) * H + m) * r;
+      float sum = 0.f;
+      for (int c = 0; c < r; c += EPC) {
+        const Chunk<DT> bc = chunk_elems<DT>(load_chunk_any<DT, VEC>(b, c, r));
+#pragma unroll
+        for (int u = 0; u < EPC; ++u)
+          if (VEC || c + u < r) sum = __builtin_fmaf(zp[c + u], Elem<DT>::to_f32(bc.v[u]), sum);
+      }
+      v += sum;
+    }
+    acc += w[p] * v;
+  }
+  out[(size_t)t * H + m] = Elem<DT>::from_f32(acc);
 }
 
 // ------------------------------------------------------------- dispatch
@@ -403,77 +488,117 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, const int *__restrict_
 // 64-row blocks (more accumulators).
 template <int TG> constexpr int unroll_for() { return TG == 1 ? 8 : 4; }
 
-template <typename DT, int TG, bool VEC, bool EK, bool LORA>
+template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
   const int cols = 16 * a.waves;
   const int ntn = (a.s.I + cols - 1) / cols;
-  hipLaunchKernelGGL((k_gate_up<DT, TG, unroll_for<TG>(), VEC, EK, LORA>),
+  hipLaunchKernelGGL((k_gate_up<DT, TG, unroll_for<TG>(), VEC, EK, MODE>),
                      dim3(ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
   return hipGetLastError();
 }
-template <typename DT, int TG, bool VEC, bool EK, bool LORA>
+template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_down(const GemmArgs &a, hipStream_t st) {
   const int cols = 16 * a.waves;
   const int ntn = (a.s.H + cols - 1) / cols;
-  hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG>(), VEC, EK, LORA>),
-                     dim3(ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
+  const int extra = MODE == 2 ? a.row_wgs : 0;
+  hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG>(), VEC, EK, MODE>),
+                     dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
   return hipGetLastError();
 }
 template <typename DT, int TG, bool VEC, bool EK, bool FROM_H>
 hipError_t go_shrink(const GemmArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H>), dim3(a.s.max_tiles),
+  hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H>), dim3(a.s.max_tiles, a.split),
                      dim3(kShrinkWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
 
 // (vec, even_k) in {(1,1), (1,0), (0,0)}: unaligned rows always mask.
-#define MOELORA_PICK(GO, DT, TG, V, L)                                               \
-  ((V).vec ? ((V).even_k ? ((L) ? GO<DT, TG, true, true, true>(a, st)                \
-                                : GO<DT, TG, true, true, false>(a, st))              \
-                         : ((L) ? GO<DT, TG, true, false, true>(a, st)               \
-                                : GO<DT, TG, true, false, false>(a, st)))            \
-           : ((L) ? GO<DT, TG, false, false, true>(a, st)                            \
-                  : GO<DT, TG, false, false, false>(a, st)))
+#define MOELORA_VEK(GO, DT, TG, V, M)                                                \
+  ((V).vec ? ((V).even_k ? GO<DT, TG, true, true, M>(a, st) : GO<DT, TG, true, false, M>(a, st)) \
+           : GO<DT, TG, false, false, M>(a, st))
 
-#define MOELORA_BY_TG(GO, V, L)                                                      \
-  switch ((V).tg) {                                                                 \
-    case 1:                                                                         \
-      return (V).bf16 ? MOELORA_PICK(GO, uint16_t, 1, V, L) : MOELORA_PICK(GO, float, 1, V, L); \
-    case 4:                                                                         \
-      return (V).bf16 ? MOELORA_PICK(GO, uint16_t, 4, V, L) : MOELORA_PICK(GO, float, 4, V, L); \
-    default:                                                                        \
-      return hipErrorInvalidValue;                                                  \
-  }
+// LoRA mode: 0 none, 1 tile-wise, 2 row-wise (16-row blocks only).
+#define MOELORA_GEMM(GO, V)                                                          \
+  do {                                                                               \
+    const int mode = !(V).lora ? 0 : (V).rowz ? 2 : 1;                                \
+    if (mode == 2 && (V).tg != 1) return hipErrorInvalidValue;                       \
+    if ((V).tg == 1) {                                                               \
+      if ((V).bf16)                                                                  \
+        return mode == 0 ? MOELORA_VEK(GO, uint16_t, 1, V, 0)                        \
+             : mode == 1 ? MOELORA_VEK(GO, uint16_t, 1, V, 1)                        \
+                         : MOELORA_VEK(GO, uint16_t, 1, V, 2);                       \
+      return mode == 0 ? MOELORA_VEK(GO, float, 1, V, 0)                             \
+           : mode == 1 ? MOELORA_VEK(GO, float, 1, V, 1)                             \
+                       : MOELORA_VEK(GO, float, 1, V, 2);                            \
+    }                                                                                \
+    if ((V).tg == 4) {                                                               \
+      if ((V).bf16)                                                                  \
+        return mode == 0 ? MOELORA_VEK(GO, uint16_t, 4, V, 0) : MOELORA_VEK(GO, uint16_t, 4, V, 1); \
+      return mode == 0 ? MOELORA_VEK(GO, float, 4, V, 0) : MOELORA_VEK(GO, float, 4, V, 1); \
+    }                                                                                \
+    return hipErrorInvalidValue;                                                     \
+  } while (0)
+
+#define MOELORA_SHRINK(V, FH)                                                        \
+  do {                                                                               \
+    if ((V).tg == 1)                                                                 \
+      return (V).bf16 ? MOELORA_VEK(go_shrink, uint16_t, 1, V, FH)                   \
+                      : MOELORA_VEK(go_shrink, float, 1, V, FH);                     \
+    if ((V).tg == 4)                                                                 \
+      return (V).bf16 ? MOELORA_VEK(go_shrink, uint16_t, 4, V, FH)                   \
+                      : MOELORA_VEK(go_shrink, float, 4, V, FH);                     \
+    return hipErrorInvalidValue;                                                     \
+  } while (0)
 
 }  // namespace
 
 hipError_t launch_gate_up(const GemmArgs &a, const GemmVariant &v, hipStream_t st) {
   if (a.s.nblk == 0) return hipSuccess;
   if (a.waves < 1 || a.waves > 4) return hipErrorInvalidValue;
-  MOELORA_BY_TG(go_gate_up, v, v.lora)
+  MOELORA_GEMM(go_gate_up, v);
 }
 
 hipError_t launch_down(const GemmArgs &a, const GemmVariant &v, hipStream_t st) {
   if (a.s.nblk == 0) return hipSuccess;
   if (a.waves < 1 || a.waves > 4) return hipErrorInvalidValue;
-  MOELORA_BY_TG(go_down, v, v.lora)
+  MOELORA_GEMM(go_down, v);
 }
 
 hipError_t launch_shrink(const GemmArgs &a, const GemmVariant &v, bool from_h, hipStream_t st) {
   if (a.s.max_tiles == 0) return hipSuccess;
-  MOELORA_BY_TG(go_shrink, v, from_h)
+  if (a.split < 1) return hipErrorInvalidValue;
+  if (from_h) MOELORA_SHRINK(v, true);
+  MOELORA_SHRINK(v, false);
 }
 
 hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const float *y,
-                          void *out, bool bf16, hipStream_t st) {
+                          void *out, bool bf16, const float *z_d, const void *B_d,
+                          const int *adapter_ids, bool vec, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
-  dim3 grid(s.T, (s.H + 1023) / 1024);
-  if (bf16)
-    hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(256), 0, st, s, ids, w, y,
-                       static_cast<uint16_t *>(out));
-  else
-    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, st, s, ids, w, y,
-                       static_cast<float *>(out));
+  if (z_d) {
+    const dim3 grid(s.T, (s.H + 63) / 64);
+#define MOELORA_COMB(DT, V)                                                                    \
+  hipLaunchKernelGGL((k_combine_rows<DT, V>), grid, dim3(64), 0, st, s, ids, w, y,             \
+                     static_cast<DT *>(out), z_d, static_cast<const DT *>(B_d), adapter_ids)
+    if (bf16) {
+      if (vec) MOELORA_COMB(uint16_t, true); else MOELORA_COMB(uint16_t, false);
+    } else {
+      if (vec) MOELORA_COMB(float, true); else MOELORA_COMB(float, false);
+    }
+#undef MOELORA_COMB
+    return hipGetLastError();
+  }
+  const dim3 grid(s.T, (s.H + 1023) / 1024);
+#define MOELORA_COMB(DT, V)                                                                    \
+  hipLaunchKernelGGL((k_combine<DT, V>), grid, dim3(256), 0, st, s, ids, w, y,                 \
+                     static_cast<DT *>(out), nullptr, nullptr, nullptr)
+  const bool v4 = s.H % 4 == 0;
+  if (bf16) {
+    if (v4) MOELORA_COMB(uint16_t, true); else MOELORA_COMB(uint16_t, false);
+  } else {
+    if (v4) MOELORA_COMB(float, true); else MOELORA_COMB(float, false);
+  }
+#undef MOELORA_COMB
   return hipGetLastError();
 }
 

@@ -33,6 +33,18 @@ struct AlignBufs {
   int *bucket_base;       // [E][NA + 1] first sorted position of the bucket
   int *tok_perm;          // [T] tokens ordered by (adapter rank, token)
   int *tok_off;           // [NA + 2] start of each adapter rank in tok_perm
+  int *row_pos;           // [R] sorted position of each routed row (small batches)
+};
+
+// Row-wise LoRA shrink riding along with another launch (small batches):
+// z[p][c] = X[row p] . A[a_p][e_p][c] for every routed row p with an adapter.
+struct RowShrinkArgs {
+  const void *x;           // gate_up: x [T][H] by token; down: h [cap][I] by position
+  const void *A;           // [NA][E][r][K]
+  float *z;                // [R][r]
+  const int *adapter_ids;  // [T]
+  int K;                   // contraction length (H or I)
+  bool vec;                // 16-byte vector loads allowed
 };
 
 // Operands of the expert GEMM kernels.  Pointers are typed void and cast to
@@ -44,8 +56,12 @@ struct GemmArgs {
   const void *W;           // base weights of this projection
   const void *A;           // LoRA A of this projection (shrink kernels)
   const void *B;           // LoRA B of this projection (expand epilogue)
-  const float *z;          // [cap][r] shrink result read by the expand
-  float *z_out;            // [cap][r] shrink result written
+  const float *z;          // [split][cap][r] shrink partial sums read by the expand,
+                           // or [R][r] per routed row (row mode)
+  float *z_out;            // [split][cap][r] shrink partial sums written
+  int split;               // workgroups sharing one shrink tile's contraction
+  RowShrinkArgs rs;        // row mode: the down shrink riding along with down
+  int row_wgs;             // row mode: leading workgroups that run rs
   int waves;               // waves per workgroup of the GEMM kernels (16 columns each)
   void *h;                 // [cap][I] SiLU(gate)*up, layer dtype
   float *y;                // [R][H] down output per routed row
@@ -57,10 +73,15 @@ constexpr int kShrinkWaves = 16;
 
 // Launchers (return hipGetLastError()).
 // Routing (when logits is non-null; results to ids_ws / w_ws) and the
-// alignment of the routed rows (caller ids when logits is null).
+// alignment of the routed rows (caller ids when logits is null).  With rs
+// non-null (small batches only) the same launch also runs the gate_up
+// shrink of every routed row.
 hipError_t launch_route_align(const Shape &s, const float *logits, const int *ids,
                               int *ids_ws, float *w_ws, const int *adapter_ids,
-                              const AlignBufs &al, hipStream_t st);
+                              const AlignBufs &al, const RowShrinkArgs *rs, bool bf16,
+                              hipStream_t st);
+// Largest routed-row count of the one-workgroup routing + alignment.
+constexpr int kSmallRows = 256;
 
 struct GemmVariant {
   bool bf16;     // element type
@@ -68,11 +89,16 @@ struct GemmVariant {
   bool vec;      // 16-byte vector loads allowed
   bool even_k;   // contraction length a multiple of the K step
   bool lora;     // expand epilogue on
+  bool rowz;     // row mode: z indexed by routed row (gate_up) / down shrink
+                 // riding along and expand moved to the combine (down)
 };
 hipError_t launch_gate_up(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
 hipError_t launch_down(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
+// Shrink of every LoRA tile (partial sums of a.split contraction splits).
 hipError_t launch_shrink(const GemmArgs &a, const GemmVariant &v, bool from_h, hipStream_t st);
+// out[t] = sum_j w[t][j] * (y[p] + [row mode] z_d[p] . B_d[a][e]^T), p = t*k + j.
 hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const float *y,
-                          void *out, bool bf16, hipStream_t st);
+                          void *out, bool bf16, const float *z_d, const void *B_d,
+                          const int *adapter_ids, bool vec, hipStream_t st);
 
 }  // namespace moelora

@@ -43,6 +43,9 @@ SMALL = [
     (16, 128, 128, 8, 4, 1, 8, "bf16", "uniform"),              # one adapter
     (16, 128, 128, 8, 4, 2, 64, "bf16", "none"),                # adapters loaded, none used
     (1, 64, 64, 4, 2, 2, 16, "bf16", "uniform"),                # one token
+    (20, 64, 96, 300, 3, 0, 0, "bf16", "none"),                 # E > 256, no adapters
+    (120, 64, 96, 300, 3, 2, 16, "bf16", "uniform_with_none"),  # E > 256, large-batch path
+    (90, 128, 64, 100, 4, 3, 16, "bf16", "uniform_with_none"),  # 64 < E <= 128
 ]
 
 
@@ -63,10 +66,11 @@ def test_small_shapes(T, H, I, E, k, NA, r, dt, ad):
     say(f"[parity] max_rel={mr:.3e} fro_rel={fr:.3e}")
 
 
-def test_caller_ids_one_expert_and_duplicates():
+@pytest.mark.parametrize("T", [40, 150])  # small and large alignment paths
+def test_caller_ids_one_expert_and_duplicates(T):
     """Caller-supplied routing: every token on expert 0 (many blocks of one
     expert, all other experts empty), plus duplicate ids within a token."""
-    w = synth.Workload("ids", T=40, H=128, I=96, E=5, k=2, NA=3, r=16, dtype="bf16",
+    w = synth.Workload("ids", T=T, H=128, I=96, E=5, k=2, NA=3, r=16, dtype="bf16",
                        adapters="uniform_with_none", seed=5)
     d = synth.make_inputs(w)
     ids = np.zeros((w.T, w.k), np.int32)
