@@ -52,12 +52,33 @@ def parse():
 
 
 def kernel_source_hash():
+    """Hash of the device-kernel sources (everything in csrc but the host
+    ABI file), used to tell whether committed counters still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lora_expert_gemm_amd", "csrc")
     for n in sorted(os.listdir(csrc)):
+        if n == "api.hip":
+            continue
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic.json), or None when there is none for this
+    workload or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source") != kernel_source_hash():
+        return None
+    for name, v in t.get("workloads", {}).get(workload, {}).items():
+        if name.startswith("k_" + kernel + "<"):
+            return v["bytes"]
+    return None
 
 
 def algorithmic(w, ids, aid):
@@ -204,7 +225,7 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": alg[f"{dom}_flop"] / dom_s / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = None if args.no_lora else measured_traffic(w.name, dom)
     roof["launch_ms"] = stage[dom]
     roof["units_per_launch"] = {"experts": alg["n_exp"], "adapter_expert_pairs": alg["n_pair"],
                                 "routed_rows": alg["R"]}

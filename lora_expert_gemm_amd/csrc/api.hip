@@ -34,6 +34,7 @@ struct moelora_plan_s {
   bool timing = false;
   int max_calls = 0, n_calls = 0;
   std::vector<hipEvent_t> ev;  // (MOELORA_N_STAGES + 1) per call
+  std::vector<unsigned> recorded;  // per call: bit i set if boundary i was recorded
 };
 
 namespace {
@@ -317,12 +318,22 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   al.tok_off = reinterpret_cast<int *>(ws + L.off_toff);
   al.row_pos = reinterpret_cast<int *>(ws + L.off_rpos);
 
+  // Stage timing: an event at the start and after every stage that launched
+  // work; a stage that launched nothing reads as 0 ms (back-to-back events
+  // are not free on the device timeline).
   hipEvent_t *ev = nullptr;
-  if (plan->timing && plan->n_calls < plan->max_calls)
+  unsigned *rec = nullptr;
+  if (plan->timing && plan->n_calls < plan->max_calls) {
+    rec = &plan->recorded[plan->n_calls];
     ev = &plan->ev[(size_t)plan->n_calls++ * (MOELORA_N_STAGES + 1)];
+    *rec = 0;
+  }
   int stage = 0;
-  auto mark = [&]() -> hipError_t {
-    return ev ? hipEventRecord(ev[stage++], st) : hipSuccess;
+  auto mark = [&](bool launched = true) -> hipError_t {
+    const int b = stage++;
+    if (!ev || !launched) return hipSuccess;
+    *rec |= 1u << b;
+    return hipEventRecord(ev[b], st);
   };
 #define MOELORA_TRY(expr)                    \
   do {                                       \
@@ -364,7 +375,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.z_out = z_gu;
     MOELORA_TRY(launch_shrink(a, variant(d, tg, d.hidden, true), false, st));
   }
-  MOELORA_TRY(mark());
+  MOELORA_TRY(mark(lora && !row));
   {
     GemmArgs a = g;
     a.W = w_gate_up;
@@ -380,7 +391,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.z_out = z_d;
     MOELORA_TRY(launch_shrink(a, variant(d, tg, d.inter, true), true, st));
   }
-  MOELORA_TRY(mark());
+  MOELORA_TRY(mark(lora && !row));
   {
     GemmArgs a = g;
     a.W = w_down;
@@ -416,6 +427,7 @@ moelora_status moelora_read_device_error(moelora_plan_t plan, const void *worksp
 moelora_status moelora_timing_begin(moelora_plan_t plan, int32_t max_calls) {
   if (!plan || max_calls < 1 || plan->timing) return MOELORA_ERR_INVALID_ARG;
   plan->ev.assign((size_t)max_calls * (MOELORA_N_STAGES + 1), nullptr);
+  plan->recorded.assign((size_t)max_calls, 0u);
   for (hipEvent_t &e : plan->ev)
     if (hipEventCreate(&e) != hipSuccess) return MOELORA_ERR_HIP;
   plan->timing = true;
@@ -432,22 +444,27 @@ moelora_status moelora_timing_end(moelora_plan_t plan, double *stage_ms, int32_t
   for (int i = 0; i < n_stages; ++i) stage_ms[i] = 0.0;
   for (int c = 0; c < plan->n_calls && rc == MOELORA_OK; ++c) {
     hipEvent_t *ev = &plan->ev[(size_t)c * (MOELORA_N_STAGES + 1)];
+    const unsigned rec = plan->recorded[c];
     if (hipEventSynchronize(ev[MOELORA_N_STAGES]) != hipSuccess) {
       rc = MOELORA_ERR_HIP;
       break;
     }
-    for (int i = 0; i < std::min(n_stages, (int)MOELORA_N_STAGES); ++i) {
+    int last = 0;  // the latest recorded boundary (boundary 0 always is)
+    for (int i = 0; i < (int)MOELORA_N_STAGES; ++i) {
+      if (!(rec >> (i + 1) & 1u)) continue;  // stage i launched nothing
       float ms = 0.f;
-      if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) {
+      if (hipEventElapsedTime(&ms, ev[last], ev[i + 1]) != hipSuccess) {
         rc = MOELORA_ERR_HIP;
         break;
       }
-      stage_ms[i] += ms;
+      if (i < n_stages) stage_ms[i] += ms;
+      last = i + 1;
     }
   }
   *n_calls = plan->n_calls;
   for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
   plan->ev.clear();
+  plan->recorded.clear();
   plan->timing = false;
   plan->max_calls = plan->n_calls = 0;
   return rc;
