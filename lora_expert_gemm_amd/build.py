@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libmoelora.so")
-SOURCES = ["api.hip", "align.hip", "expert_gemm.hip"]
+SOURCES = ["api.hip", "align.hip", "expert_gemm.hip", "tiled_gemm.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

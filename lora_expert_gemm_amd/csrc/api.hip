@@ -40,15 +40,23 @@ struct moelora_plan_s {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kTgSmall = 1, kTgLarge = 4;
+constexpr int kTgSmall = 1, kTgLarge = 4, kTgTiled = 8;
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Token-count bucket: blocks of 16 rows while an expert gets about one
-// block of rows, else blocks of 64.
+// block of rows (weight streaming), blocks of 128 rows for the LDS-tiled
+// MFMA kernels once experts average 64 rows or more (bf16 with 16-byte
+// aligned rows), else blocks of 64.
+bool tiled_ok(const moelora_desc &d) {
+  return d.dtype == MOELORA_BF16 && d.hidden % 8 == 0 && d.inter % 8 == 0 && d.rank % 8 == 0;
+}
+bool tiled_shrink_ok(const moelora_desc &d) { return d.rank <= 64; }
 int choose_tg(const moelora_desc &d, int T) {
   const long long rows = (long long)T * d.top_k;
-  return rows <= 24LL * d.n_experts ? kTgSmall : kTgLarge;
+  if (rows <= 24LL * d.n_experts) return kTgSmall;
+  if (tiled_ok(d) && rows >= 64LL * d.n_experts) return kTgTiled;
+  return kTgLarge;
 }
 
 // Waves (16 output columns each) per GEMM workgroup.  The decode weight
@@ -201,16 +209,19 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   moelora_plan_s *p = new (std::nothrow) moelora_plan_s();
   if (!p) return MOELORA_ERR_INVALID_ARG;
   p->d = *desc;
-  // the largest layout over every token count up to max_tokens: sizes grow
-  // with T inside a bucket, so the top of each bucket bounds it
+  // the largest layout over every token count up to max_tokens: buckets
+  // are contiguous ranges of T and sizes grow with T inside a bucket, so the
+  // last T of each bucket bounds it
   size_t ws = make_layout(p->d, p->d.max_tokens).total;
-  int lo = 0, hi = p->d.max_tokens;
-  if (choose_tg(p->d, hi) != kTgSmall) {  // top of the small bucket
+  for (int T = p->d.max_tokens; T > 0;) {
+    const int tg = choose_tg(p->d, T);
+    int lo = 0, hi = T;  // smallest T' with the same bucket as T
     while (lo < hi) {
-      int mid = lo + (hi - lo + 1) / 2;
-      if (choose_tg(p->d, mid) == kTgSmall) lo = mid; else hi = mid - 1;
+      const int mid = lo + (hi - lo) / 2;
+      if (choose_tg(p->d, mid) == tg) hi = mid; else lo = mid + 1;
     }
-    ws = std::max(ws, make_layout(p->d, lo).total);
+    ws = std::max(ws, make_layout(p->d, T).total);
+    T = lo - 1;
   }
   p->ws_bytes = ws;
   // tuning sweeps only: force the waves per GEMM workgroup (1..4)
@@ -373,7 +384,9 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     GemmArgs a = g;
     a.A = lora_a_gu;
     a.z_out = z_gu;
-    MOELORA_TRY(launch_shrink(a, variant(d, tg, d.hidden, true), false, st));
+    MOELORA_TRY(tg == kTgTiled && tiled_shrink_ok(d)
+                    ? launch_tiled_shrink(a, false, st)
+                    : launch_shrink(a, variant(d, tg, d.hidden, true), false, st));
   }
   MOELORA_TRY(mark(lora && !row));
   {
@@ -382,14 +395,16 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.B = lora_b_gu;
     a.z = z_gu;
     a.waves = waves_gu;
-    MOELORA_TRY(launch_gate_up(a, vg, st));
+    MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, true, vg, st) : launch_gate_up(a, vg, st));
   }
   MOELORA_TRY(mark());
   if (lora && !row) {
     GemmArgs a = g;
     a.A = lora_a_d;
     a.z_out = z_d;
-    MOELORA_TRY(launch_shrink(a, variant(d, tg, d.inter, true), true, st));
+    MOELORA_TRY(tg == kTgTiled && tiled_shrink_ok(d)
+                    ? launch_tiled_shrink(a, true, st)
+                    : launch_shrink(a, variant(d, tg, d.inter, true), true, st));
   }
   MOELORA_TRY(mark(lora && !row));
   {
@@ -402,7 +417,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
       a.rs = RowShrinkArgs{h, lora_a_d, z_d, adapter_ids, d.inter, vd.vec};
       a.row_wgs = s.R;
     }
-    MOELORA_TRY(launch_down(a, vd, st));
+    MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, false, vd, st) : launch_down(a, vd, st));
   }
   MOELORA_TRY(mark());
   MOELORA_TRY(launch_combine(s, ids, wts, g.y, out, d.dtype == MOELORA_BF16, row ? z_d : nullptr,

@@ -547,6 +547,7 @@ hipError_t go_shrink(const GemmArgs &a, hipStream_t st) {
     if ((V).tg == 4)                                                                 \
       return (V).bf16 ? MOELORA_VEK(go_shrink, uint16_t, 4, V, FH)                   \
                       : MOELORA_VEK(go_shrink, float, 4, V, FH);                     \
+    if ((V).tg == 8 && (V).bf16) return MOELORA_VEK(go_shrink, uint16_t, 8, V, FH);  \
     return hipErrorInvalidValue;                                                     \
   } while (0)
 

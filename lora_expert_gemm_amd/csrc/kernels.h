@@ -93,6 +93,10 @@ struct GemmVariant {
                  // riding along and expand moved to the combine (down)
 };
 hipError_t launch_gate_up(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
+// LDS-tiled MFMA GEMM for 128-row blocks (bf16, 16-byte aligned rows).
+hipError_t launch_tiled(const GemmArgs &a, bool gate_up, const GemmVariant &v, hipStream_t st);
+// LDS-tiled LoRA shrink for 128-row blocks (bf16, r <= 64, r % 8 == 0, split 1).
+hipError_t launch_tiled_shrink(const GemmArgs &a, bool from_h, hipStream_t st);
 hipError_t launch_down(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
 // Shrink of every LoRA tile (partial sums of a.split contraction splits).
 hipError_t launch_shrink(const GemmArgs &a, const GemmVariant &v, bool from_h, hipStream_t st);

@@ -1,0 +1,409 @@
+// LDS-tiled grouped expert GEMMs for large batches (hundreds of rows per
+// expert), where the layer is bound by the matrix cores, not by HBM.
+//
+// Same computation as the streaming kernels in expert_gemm.hip: the grouped
+// gate_up / down GEMMs of the AWS ML blog "Efficiently serve dozens of
+// fine-tuned models with vLLM on Amazon SageMaker AI and Amazon Bedrock",
+// section "Implementing multi-LoRA inference for MoE models in vLLM" (one
+// GEMM per expert), with the LoRA expand added into the base accumulators
+// (section "Kernel optimizations").
+//
+// Workgroup tile: 128 tokens (one alignment block) x 256 weight rows, 4
+// waves.  gate_up: rows 0..127 of the weight tile are gate rows n0..n0+127,
+// rows 128..255 the matching up rows, so wave w holds gate and up for
+// h-columns n0 + 32w .. +31 and forms SiLU(gate)*up in registers.  down:
+// wave w holds output rows m0 + 64w .. +63.  Each wave: 2 weight tiles x 4
+// token tiles of v_mfma_f32_32x32x16_bf16 (weights on the 32-row side).
+//
+// The contraction is staged through LDS in BK-wide slabs, double buffered:
+// the global loads of slab s+1 are issued (into registers) before the MFMAs
+// of slab s and written to the other LDS buffer after them; one barrier per
+// slab.  LDS rows are BK*2 bytes; the 16-byte chunk c of row r is stored at
+// chunk c ^ ((r / rows_per_128B) % chunks_per_row) so that the 32 rows a
+// fragment read touches fall on distinct banks.
+#include "common.h"
+#include "kernels.h"
+
+namespace moelora {
+
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kTM = 128;   // tokens per workgroup tile (= block size)
+constexpr int kTW = 256;   // weight rows per workgroup tile
+constexpr int kTWaves = 4;
+constexpr int kTThreads = kTWaves * kWave;
+
+__device__ __forceinline__ void mma32(f32x16_t &c, u32x4_t a, u32x4_t b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                              __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int BK>
+struct Lds {
+  static constexpr int kCpr = BK / 8;                // 16-byte chunks per row
+  static constexpr int kRpl = 8 / kCpr;              // rows per 128-byte line
+  static constexpr int kABytes = kTW * BK * 2;
+  static constexpr int kBBytes = kTM * BK * 2;
+  static constexpr int kStage = kABytes + kBBytes;
+  __device__ static int off(int row, int c) {
+    return row * (BK * 2) + ((c ^ ((row / kRpl) % kCpr)) << 4);
+  }
+};
+
+template <bool GATE_UP, int BK, bool EVEN_K, bool LORA>
+__global__ __launch_bounds__(kTThreads, 1) void k_tiled(GemmArgs a) {
+  using L = Lds<BK>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Shape &s = a.s;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int li = lane & 31, lh = lane >> 5;
+
+  const int Lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int blk = Lid % s.nblk, nt = Lid / s.nblk;
+  const int e = a.al.block_expert[blk];
+  if (e < 0) return;
+  const int I = s.I, H = s.H;
+  const int K = GATE_UP ? H : I;
+  const int Nout = GATE_UP ? I : H;              // valid output columns of this projection
+  const int n0 = nt * (GATE_UP ? kTW / 2 : kTW);  // first output column of the tile
+
+  // ---- per-thread global load plan: thread t loads chunk (t % kCpr) of
+  // rows t / kCpr + j * (kTThreads / kCpr)
+  constexpr int kRowStep = kTThreads / L::kCpr;
+  constexpr int kALoads = kTW / kRowStep, kBLoads = kTM / kRowStep;
+  const int lc = tid % L::kCpr, lr = tid / L::kCpr;
+  const uint16_t *W = static_cast<const uint16_t *>(a.W);
+  const uint16_t *arow[kALoads];
+#pragma unroll
+  for (int j = 0; j < kALoads; ++j) {
+    const int r = lr + j * kRowStep;  // weight-tile row
+    int wrow;
+    if (GATE_UP) {
+      const int col = min(n0 + (r & (kTW / 2 - 1)), I - 1);
+      wrow = (r < kTW / 2 ? 0 : I) + col;
+      arow[j] = W + ((size_t)e * 2 * I + wrow) * K;
+    } else {
+      wrow = min(n0 + r, H - 1);
+      arow[j] = W + ((size_t)e * H + wrow) * K;
+    }
+  }
+  const uint16_t *brow[kBLoads];
+  bool bok[kBLoads];
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) {
+    const int r = lr + j * kRowStep;
+    const int pos = blk * kTM + r;
+    const int p = a.al.sorted_rows[pos];
+    bok[j] = p < s.R;
+    if (GATE_UP)
+      brow[j] = static_cast<const uint16_t *>(a.x) + (size_t)(bok[j] ? p / s.k : 0) * H;
+    else
+      brow[j] = static_cast<const uint16_t *>(a.h) + (size_t)pos * I;
+  }
+
+  u32x4_t ra[kALoads], rb[kBLoads];
+  auto gload = [&](int ks) {
+    const int k = ks * BK + lc * 8;
+#pragma unroll
+    for (int j = 0; j < kALoads; ++j)
+      ra[j] = EVEN_K ? load_chunk(arow[j], k) : load_chunk_any<uint16_t, true>(arow[j], k, K);
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j) {
+      rb[j] = u32x4_t{0, 0, 0, 0};
+      if (bok[j]) rb[j] = EVEN_K ? load_chunk(brow[j], k) : load_chunk_any<uint16_t, true>(brow[j], k, K);
+    }
+  };
+  auto lstore = [&](int buf) {
+    unsigned char *sa = smem + buf * L::kStage, *sb = sa + L::kABytes;
+#pragma unroll
+    for (int j = 0; j < kALoads; ++j)
+      *reinterpret_cast<u32x4_t *>(sa + L::off(lr + j * kRowStep, lc)) = ra[j];
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j)
+      *reinterpret_cast<u32x4_t *>(sb + L::off(lr + j * kRowStep, lc)) = rb[j];
+  };
+
+  // wave's weight tiles (rows within the 256-row tile) and token tiles
+  const int wt0 = GATE_UP ? wave * 32 : wave * 64;
+  const int wt1 = GATE_UP ? kTW / 2 + wave * 32 : wave * 64 + 32;
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[i][b] = f32x16_t{};
+
+  const int nks = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nks) gload(ks + 1);
+    const unsigned char *sa = smem + buf * L::kStage, *sb = sa + L::kABytes;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = 2 * kk + lh;  // this lane's 16-byte chunk of the slab
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(sa + L::off(wt0 + li, c));
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(sa + L::off(wt1 + li, c));
+      u32x4_t bt[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        bt[b] = *reinterpret_cast<const u32x4_t *>(sb + L::off(b * 32 + li, c));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        mma32(acc[0][b], a0, bt[b]);
+        mma32(acc[1][b], a1, bt[b]);
+      }
+    }
+    if (ks + 1 < nks) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- LoRA expand: acc += B_rows . z^T for each LoRA tile of the block
+  if (LORA) {
+    const int r = s.r;
+    const uint16_t *Bm = static_cast<const uint16_t *>(a.B);
+    const int t0 = a.al.block_tile_start[blk], t1 = a.al.block_tile_start[blk + 1];
+    const size_t stride = (size_t)s.cap * r;
+    for (int ti = t0; ti < t1; ++ti) {
+      const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[ti];
+      const int ad = tl.y, lo = tl.z, n = tl.w;
+      const uint16_t *bw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int wr = (i == 0 ? wt0 : wt1) + li;
+        int row;
+        if (GATE_UP) row = (wr < kTW / 2 ? 0 : I) + min(n0 + (wr & (kTW / 2 - 1)), I - 1);
+        else row = min(n0 + wr, H - 1);
+        bw[i] = Bm + (((size_t)ad * s.E + e) * (GATE_UP ? 2 * I : H) + row) * r;
+      }
+      for (int kc = 0; kc < r; kc += 16) {
+        const int kk = kc + lh * 8;
+        const u32x4_t c0 = load_chunk_any<uint16_t, true>(bw[0], kk, r);
+        const u32x4_t c1 = load_chunk_any<uint16_t, true>(bw[1], kk, r);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int local = b * 32 + li;
+          float zv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zv[q] = 0.f;
+          if (local >= lo && local < lo + n && kk < r) {
+            const float *zp = a.z + ((size_t)blk * kTM + local) * r + kk;
+            for (int sp = 0; sp < a.split; ++sp) {
+              const float4 v0 = *reinterpret_cast<const float4 *>(zp + sp * stride);
+              const float4 v1 = *reinterpret_cast<const float4 *>(zp + sp * stride + 4);
+              zv[0] += v0.x, zv[1] += v0.y, zv[2] += v0.z, zv[3] += v0.w;
+              zv[4] += v1.x, zv[5] += v1.y, zv[6] += v1.z, zv[7] += v1.w;
+            }
+          }
+          u32x4_t zh, zl;
+          SplitF32<uint16_t>::run(zv, zh, zl);
+          mma32(acc[0][b], c0, zh);
+          mma32(acc[0][b], c0, zl);
+          mma32(acc[1][b], c1, zh);
+          mma32(acc[1][b], c1, zl);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue.  Lane holds, for token tile b, token column 32 b + li and
+  // weight rows 8 (v / 4) + 4 lh + v % 4 of each of its two weight tiles.
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int pos = blk * kTM + b * 32 + li;
+    const int p = a.al.sorted_rows[pos];
+    if (p >= s.R) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int wr = 8 * g + 4 * lh;  // first of 4 consecutive rows in the wave's tile
+      if (GATE_UP) {
+        const int col = n0 + wt0 + wr;  // h column
+        uint16_t hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          hv[v] = f32_to_bf16(silu_f32(acc[0][b][4 * g + v]) * acc[1][b][4 * g + v]);
+        uint16_t *dst = static_cast<uint16_t *>(a.h) + (size_t)pos * I + col;
+        if (col + 3 < Nout) {
+          *reinterpret_cast<uint2 *>(dst) = __builtin_bit_cast(uint2, hv);
+        } else {
+          for (int v = 0; v < 4; ++v)
+            if (col + v < Nout) dst[v] = hv[v];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int m = n0 + (i == 0 ? wt0 : wt1) + wr;
+          float *dst = a.y + (size_t)p * H + m;
+          if (m + 3 < Nout) {
+            *reinterpret_cast<float4 *>(dst) =
+                make_float4(acc[i][b][4 * g], acc[i][b][4 * g + 1], acc[i][b][4 * g + 2],
+                            acc[i][b][4 * g + 3]);
+          } else {
+            for (int v = 0; v < 4; ++v)
+              if (m + v < Nout) dst[v] = acc[i][b][4 * g + v];
+          }
+        }
+      }
+    }
+  }
+}
+
+// LoRA shrink for 128-row blocks: z[pos][c] = X[pos] . A[a][e][c] for the
+// rows of one LoRA tile (one workgroup per tile), X = x by token (gate_up)
+// or h by position (down).  A (r <= 64 rows, padded to 64) and the block's
+// 128 token rows are staged through LDS like the GEMM above; wave w takes
+// token tile w against both 32-row halves of A.  Rows outside the tile's
+// run load zeros.  One workgroup covers the whole contraction, so z is
+// final (no partial sums).
+template <bool FROM_H, int BK, bool EVEN_K>
+__global__ __launch_bounds__(kTThreads) void k_tiled_shrink(GemmArgs a) {
+  using L = Lds<BK>;
+  constexpr int kAR = 64;  // A rows staged (r <= 64)
+  constexpr int kABytes = kAR * BK * 2, kStage = kABytes + L::kBBytes;
+  __shared__ __align__(16) unsigned char smem[2 * kStage];
+  const Shape &s = a.s;
+  const int tile = blockIdx.x;
+  if (tile >= a.al.counts[2]) return;
+  const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[tile];
+  const int blk = tl.x, ad = tl.y, lo = tl.z, n = tl.w;
+  const int e = a.al.block_expert[blk];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int li = lane & 31, lh = lane >> 5;
+  const int r = s.r;
+  const int K = FROM_H ? s.I : s.H;
+
+  constexpr int kRowStep = kTThreads / L::kCpr;
+  constexpr int kALoads = kAR / kRowStep, kBLoads = kTM / kRowStep;
+  const int lc = tid % L::kCpr, lr = tid / L::kCpr;
+  const uint16_t *arow[kALoads];
+#pragma unroll
+  for (int j = 0; j < kALoads; ++j)
+    arow[j] = static_cast<const uint16_t *>(a.A) +
+              (((size_t)ad * s.E + e) * r + min(lr + j * kRowStep, r - 1)) * K;
+  const uint16_t *brow[kBLoads];
+  bool bok[kBLoads];
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) {
+    const int rr = lr + j * kRowStep;
+    const int pos = blk * kTM + rr;
+    bok[j] = rr >= lo && rr < lo + n;
+    if (FROM_H) {
+      brow[j] = static_cast<const uint16_t *>(a.h) + (size_t)pos * s.I;
+    } else {
+      const int p = bok[j] ? a.al.sorted_rows[pos] : 0;
+      brow[j] = static_cast<const uint16_t *>(a.x) + (size_t)(p / s.k) * s.H;
+    }
+  }
+  u32x4_t ra[kALoads], rb[kBLoads];
+  auto gload = [&](int ks) {
+    const int k = ks * BK + lc * 8;
+#pragma unroll
+    for (int j = 0; j < kALoads; ++j)
+      ra[j] = EVEN_K ? load_chunk(arow[j], k) : load_chunk_any<uint16_t, true>(arow[j], k, K);
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j) {
+      rb[j] = u32x4_t{0, 0, 0, 0};
+      if (bok[j]) rb[j] = EVEN_K ? load_chunk(brow[j], k) : load_chunk_any<uint16_t, true>(brow[j], k, K);
+    }
+  };
+  auto lstore = [&](int buf) {
+    unsigned char *sa = smem + buf * kStage, *sb = sa + kABytes;
+#pragma unroll
+    for (int j = 0; j < kALoads; ++j)
+      *reinterpret_cast<u32x4_t *>(sa + L::off(lr + j * kRowStep, lc)) = ra[j];
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j)
+      *reinterpret_cast<u32x4_t *>(sb + L::off(lr + j * kRowStep, lc)) = rb[j];
+  };
+
+  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+  const int nks = (K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nks) gload(ks + 1);
+    const unsigned char *sa = smem + buf * kStage, *sb = sa + kABytes;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = 2 * kk + lh;
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(sa + L::off(li, c));
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(sa + L::off(32 + li, c));
+      const u32x4_t bt = *reinterpret_cast<const u32x4_t *>(sb + L::off(wave * 32 + li, c));
+      mma32(acc[0], a0, bt);
+      mma32(acc[1], a1, bt);
+    }
+    if (ks + 1 < nks) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  // lane: token column wave*32 + li; A rows 32 i + 8 (v/4) + 4 lh + v%4
+  const int local = wave * 32 + li;
+  if (local < lo || local >= lo + n) return;
+  float *zrow = a.z_out + ((size_t)blk * kTM + local) * r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * i + 8 * g + 4 * lh;
+      if (c + 3 < r) {
+        *reinterpret_cast<float4 *>(zrow + c) =
+            make_float4(acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]);
+      } else {
+        for (int v = 0; v < 4; ++v)
+          if (c + v < r) zrow[c + v] = acc[i][4 * g + v];
+      }
+    }
+}
+
+template <bool GATE_UP, int BK, bool EVEN_K, bool LORA>
+hipError_t go_tiled(const GemmArgs &a, hipStream_t st) {
+  const int cols = GATE_UP ? kTW / 2 : kTW;
+  const int ntn = ((GATE_UP ? a.s.I : a.s.H) + cols - 1) / cols;
+  const size_t lds = 2 * (size_t)Lds<BK>::kStage;
+  auto kern = k_tiled<GATE_UP, BK, EVEN_K, LORA>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(ntn * a.s.nblk), dim3(kTThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <bool GATE_UP>
+hipError_t pick_tiled(const GemmArgs &a, bool even_k, bool lora, hipStream_t st) {
+  constexpr int BK = 64;
+  if (even_k) return lora ? go_tiled<GATE_UP, BK, true, true>(a, st) : go_tiled<GATE_UP, BK, true, false>(a, st);
+  return lora ? go_tiled<GATE_UP, BK, false, true>(a, st) : go_tiled<GATE_UP, BK, false, false>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_tiled_shrink(const GemmArgs &a, bool from_h, hipStream_t st) {
+  if (a.s.max_tiles == 0) return hipSuccess;
+  if (a.s.BM != kTM || a.s.r > 64 || a.s.r % 8 != 0 || a.split != 1) return hipErrorInvalidValue;
+  const int K = from_h ? a.s.I : a.s.H;
+  const bool even = K % 64 == 0;
+#define MOELORA_TS(FH, EV) \
+  hipLaunchKernelGGL((k_tiled_shrink<FH, 64, EV>), dim3(a.s.max_tiles), dim3(kTThreads), 0, st, a)
+  if (from_h) {
+    if (even) MOELORA_TS(true, true); else MOELORA_TS(true, false);
+  } else {
+    if (even) MOELORA_TS(false, true); else MOELORA_TS(false, false);
+  }
+#undef MOELORA_TS
+  return hipGetLastError();
+}
+
+hipError_t launch_tiled(const GemmArgs &a, bool gate_up, const GemmVariant &v, hipStream_t st) {
+  if (a.s.nblk == 0) return hipSuccess;
+  if (!v.bf16 || !v.vec || a.s.BM != kTM) return hipErrorInvalidValue;
+  const int K = gate_up ? a.s.H : a.s.I;
+  const bool even_k = K % 64 == 0;
+  return gate_up ? pick_tiled<true>(a, even_k, v.lora, st) : pick_tiled<false>(a, even_k, v.lora, st);
+}
+
+}  // namespace moelora

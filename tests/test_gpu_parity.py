@@ -46,6 +46,9 @@ SMALL = [
     (20, 64, 96, 300, 3, 0, 0, "bf16", "none"),                 # E > 256, no adapters
     (120, 64, 96, 300, 3, 2, 16, "bf16", "uniform_with_none"),  # E > 256, large-batch path
     (90, 128, 64, 100, 4, 3, 16, "bf16", "uniform_with_none"),  # 64 < E <= 128
+    (300, 256, 320, 4, 2, 3, 16, "bf16", "uniform_with_none"),  # LDS-tiled, partial column tile
+    (260, 200, 136, 4, 2, 2, 32, "bf16", "uniform_with_none"),  # LDS-tiled, K % 64 != 0
+    (512, 128, 128, 2, 1, 0, 0, "bf16", "none"),                # LDS-tiled, no adapters
 ]
 
 
