@@ -30,6 +30,7 @@ struct moelora_plan_s {
   moelora_desc d;
   size_t ws_bytes;
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
+  int tiled_bk = 32;                                 // LDS-tiled slab width
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -227,6 +228,7 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   // tuning sweeps only: force the waves per GEMM workgroup (1..4)
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
+  if (const char *v = getenv("MOELORA_TILED_BK")) p->tiled_bk = atoi(v) == 64 ? 64 : 32;
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -374,6 +376,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   GemmArgs g{};
   g.s = s;
   g.split = L.split;
+  g.tiled_bk = plan->tiled_bk;
   g.topk_ids = ids;
   g.x = x;
   g.al = al;

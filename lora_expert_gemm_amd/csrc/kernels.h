@@ -63,6 +63,7 @@ struct GemmArgs {
   RowShrinkArgs rs;        // row mode: the down shrink riding along with down
   int row_wgs;             // row mode: leading workgroups that run rs
   int waves;               // waves per workgroup of the GEMM kernels (16 columns each)
+  int tiled_bk;            // LDS-tiled kernels: contraction slab (32 or 64)
   void *h;                 // [cap][I] SiLU(gate)*up, layer dtype
   float *y;                // [R][H] down output per routed row
   AlignBufs al;

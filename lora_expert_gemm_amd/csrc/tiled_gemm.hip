@@ -18,9 +18,7 @@
 // The contraction is staged through LDS in BK-wide slabs, double buffered:
 // the global loads of slab s+1 are issued (into registers) before the MFMAs
 // of slab s and written to the other LDS buffer after them; one barrier per
-// slab.  LDS rows are BK*2 bytes; the 16-byte chunk c of row r is stored at
-// chunk c ^ ((r / rows_per_128B) % chunks_per_row) so that the 32 rows a
-// fragment read touches fall on distinct banks.
+// slab.  LDS rows are BK*2 bytes with XOR-swizzled 16-byte chunks.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,13 +45,19 @@ struct Lds {
   static constexpr int kABytes = kTW * BK * 2;
   static constexpr int kBBytes = kTM * BK * 2;
   static constexpr int kStage = kABytes + kBBytes;
+  // The chunk index is XOR-swizzled by (row / kRpl + row / 8) % kCpr: the
+  // 16 consecutive rows that 16 lanes read at one logical chunk then fall
+  // on 16 distinct 16-byte bank groups of a 256-byte window (and 8 rows on
+  // 8 groups of a 128-byte window), and a row's chunks stay a permutation.
   __device__ static int off(int row, int c) {
-    return row * (BK * 2) + ((c ^ ((row / kRpl) % kCpr)) << 4);
+    return row * (BK * 2) + ((c ^ ((row / kRpl + row / 8) % kCpr)) << 4);
   }
 };
 
+// BK = 32 halves the LDS footprint (48 KB) so that two workgroups share a
+// CU and hide each other's slab loads and barriers.
 template <bool GATE_UP, int BK, bool EVEN_K, bool LORA>
-__global__ __launch_bounds__(kTThreads, 1) void k_tiled(GemmArgs a) {
+__global__ __launch_bounds__(kTThreads, BK == 32 ? 2 : 1) void k_tiled(GemmArgs a) {
   using L = Lds<BK>;
   extern __shared__ __align__(16) unsigned char smem[];
   const Shape &s = a.s;
@@ -103,26 +107,30 @@ __global__ __launch_bounds__(kTThreads, 1) void k_tiled(GemmArgs a) {
       brow[j] = static_cast<const uint16_t *>(a.h) + (size_t)pos * I;
   }
 
-  u32x4_t ra[kALoads], rb[kBLoads];
-  auto gload = [&](int ks) {
+  // register staging of one slab: loaded while the previous slab's MFMAs run
+  struct Stage {
+    u32x4_t a[kALoads], b[kBLoads];
+  };
+  Stage st;
+  auto gload = [&](Stage &g, int ks) {
     const int k = ks * BK + lc * 8;
 #pragma unroll
     for (int j = 0; j < kALoads; ++j)
-      ra[j] = EVEN_K ? load_chunk(arow[j], k) : load_chunk_any<uint16_t, true>(arow[j], k, K);
+      g.a[j] = EVEN_K ? load_chunk(arow[j], k) : load_chunk_any<uint16_t, true>(arow[j], k, K);
 #pragma unroll
     for (int j = 0; j < kBLoads; ++j) {
-      rb[j] = u32x4_t{0, 0, 0, 0};
-      if (bok[j]) rb[j] = EVEN_K ? load_chunk(brow[j], k) : load_chunk_any<uint16_t, true>(brow[j], k, K);
+      g.b[j] = u32x4_t{0, 0, 0, 0};
+      if (bok[j]) g.b[j] = EVEN_K ? load_chunk(brow[j], k) : load_chunk_any<uint16_t, true>(brow[j], k, K);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const Stage &g, int buf) {
     unsigned char *sa = smem + buf * L::kStage, *sb = sa + L::kABytes;
 #pragma unroll
     for (int j = 0; j < kALoads; ++j)
-      *reinterpret_cast<u32x4_t *>(sa + L::off(lr + j * kRowStep, lc)) = ra[j];
+      *reinterpret_cast<u32x4_t *>(sa + L::off(lr + j * kRowStep, lc)) = g.a[j];
 #pragma unroll
     for (int j = 0; j < kBLoads; ++j)
-      *reinterpret_cast<u32x4_t *>(sb + L::off(lr + j * kRowStep, lc)) = rb[j];
+      *reinterpret_cast<u32x4_t *>(sb + L::off(lr + j * kRowStep, lc)) = g.b[j];
   };
 
   // wave's weight tiles (rows within the 256-row tile) and token tiles
@@ -135,30 +143,40 @@ __global__ __launch_bounds__(kTThreads, 1) void k_tiled(GemmArgs a) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[i][b] = f32x16_t{};
 
+  // MFMAs of one slab from LDS buffer buf; fragments of k-step kk + 1 are
+  // read while the MFMAs of kk run
+  auto compute = [&](int buf) {
+    const unsigned char *sa = smem + buf * L::kStage, *sb = sa + L::kABytes;
+    u32x4_t fa[2][2], fb[2][4];
+    auto fread = [&](int kk, int slot) {
+      const int c = 2 * kk + lh;  // this lane's 16-byte chunk of the slab
+      fa[slot][0] = *reinterpret_cast<const u32x4_t *>(sa + L::off(wt0 + li, c));
+      fa[slot][1] = *reinterpret_cast<const u32x4_t *>(sa + L::off(wt1 + li, c));
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        fb[slot][b] = *reinterpret_cast<const u32x4_t *>(sb + L::off(b * 32 + li, c));
+    };
+    fread(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) fread(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        mma32(acc[0][b], fa[kk & 1][0], fb[kk & 1][b]);
+        mma32(acc[1][b], fa[kk & 1][1], fb[kk & 1][b]);
+      }
+    }
+  };
+
   const int nks = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
+  gload(st, 0);
+  lstore(st, 0);
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < nks) gload(ks + 1);
-    const unsigned char *sa = smem + buf * L::kStage, *sb = sa + L::kABytes;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = 2 * kk + lh;  // this lane's 16-byte chunk of the slab
-      const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(sa + L::off(wt0 + li, c));
-      const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(sa + L::off(wt1 + li, c));
-      u32x4_t bt[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        bt[b] = *reinterpret_cast<const u32x4_t *>(sb + L::off(b * 32 + li, c));
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        mma32(acc[0][b], a0, bt[b]);
-        mma32(acc[1][b], a1, bt[b]);
-      }
-    }
-    if (ks + 1 < nks) lstore(buf ^ 1);
+    if (ks + 1 < nks) gload(st, ks + 1);
+    compute(buf);
+    if (ks + 1 < nks) lstore(st, buf ^ 1);
     __syncthreads();
   }
 
@@ -373,9 +391,8 @@ hipError_t go_tiled(const GemmArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool GATE_UP>
+template <bool GATE_UP, int BK>
 hipError_t pick_tiled(const GemmArgs &a, bool even_k, bool lora, hipStream_t st) {
-  constexpr int BK = 64;
   if (even_k) return lora ? go_tiled<GATE_UP, BK, true, true>(a, st) : go_tiled<GATE_UP, BK, true, false>(a, st);
   return lora ? go_tiled<GATE_UP, BK, false, true>(a, st) : go_tiled<GATE_UP, BK, false, false>(a, st);
 }
@@ -402,8 +419,11 @@ hipError_t launch_tiled(const GemmArgs &a, bool gate_up, const GemmVariant &v, h
   if (a.s.nblk == 0) return hipSuccess;
   if (!v.bf16 || !v.vec || a.s.BM != kTM) return hipErrorInvalidValue;
   const int K = gate_up ? a.s.H : a.s.I;
-  const bool even_k = K % 64 == 0;
-  return gate_up ? pick_tiled<true>(a, even_k, v.lora, st) : pick_tiled<false>(a, even_k, v.lora, st);
+  const int bk = a.tiled_bk == 64 ? 64 : 32;
+  const bool even_k = K % bk == 0;
+  if (bk == 64)
+    return gate_up ? pick_tiled<true, 64>(a, even_k, v.lora, st) : pick_tiled<false, 64>(a, even_k, v.lora, st);
+  return gate_up ? pick_tiled<true, 32>(a, even_k, v.lora, st) : pick_tiled<false, 32>(a, even_k, v.lora, st);
 }
 
 }  // namespace moelora
