@@ -30,7 +30,8 @@ struct moelora_plan_s {
   moelora_desc d;
   size_t ws_bytes;
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
-  int tiled_bk = 32;                                 // LDS-tiled slab width
+  int raster_gb = 0;
+  int tiled_bk = 0;  // tiled GEMM: 0 = 8-wave kernel where K % 64 == 0; 32 / 64 = 4-wave slab width
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -53,6 +54,11 @@ bool tiled_ok(const moelora_desc &d) {
   return d.dtype == MOELORA_BF16 && d.hidden % 8 == 0 && d.inter % 8 == 0 && d.rank % 8 == 0;
 }
 bool tiled_shrink_ok(const moelora_desc &d) { return d.rank <= 64; }
+// The 8-wave tiled GEMM takes the LoRA expand as extra contraction slabs:
+// needs 64-wide slabs of the base contraction K and of (z hi | z lo) (2r).
+bool fused_lora_ok(const moelora_desc &d, int K) {
+  return tiled_shrink_ok(d) && d.rank % 32 == 0 && K % 64 == 0;
+}
 int choose_tg(const moelora_desc &d, int T) {
   const long long rows = (long long)T * d.top_k;
   if (rows <= 24LL * d.n_experts) return kTgSmall;
@@ -79,8 +85,8 @@ struct Layout {
   Shape s;
   int waves_gu, waves_d, split;
   size_t off_error, off_counts, off_ids, off_w, off_sorted, off_bexp, off_seg, off_lseg,
-      off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_rpos, off_zgu, off_zd,
-      off_h, off_y, total;
+      off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_rpos, off_zero, off_zgu,
+      off_zd, off_h, off_y, total;
 };
 
 Layout make_layout(const moelora_desc &d, int T) {
@@ -128,7 +134,9 @@ Layout make_layout(const moelora_desc &d, int T) {
   L.off_tperm = take(4ull * T);
   L.off_toff = take(4ull * (s.NA + 2));
   L.off_rpos = take(4ull * s.R);
-  // z: tile-wise [split][cap][r] partial sums, or row-wise [R][r] (R <= cap)
+  L.off_zero = take(128);
+  // z: tile-wise [split][cap][r] partial sums (or, same size with split 1,
+  // bf16 [cap][2r] hi | lo rows), or row-wise [R][r] (R <= cap)
   L.off_zgu = take(4ull * L.split * s.cap * s.r);
   L.off_zd = take(4ull * L.split * s.cap * s.r);
   L.off_h = take(es * s.cap * s.I);
@@ -228,7 +236,8 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   // tuning sweeps only: force the waves per GEMM workgroup (1..4)
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
-  if (const char *v = getenv("MOELORA_TILED_BK")) p->tiled_bk = atoi(v) == 64 ? 64 : 32;
+  if (const char *v = getenv("MOELORA_RASTER_GB")) p->raster_gb = std::max(0, atoi(v));
+  if (const char *v = getenv("MOELORA_TILED_BK")) p->tiled_bk = atoi(v) == 64 ? 64 : atoi(v) == 32 ? 32 : 0;
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -377,6 +386,11 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   g.s = s;
   g.split = L.split;
   g.tiled_bk = plan->tiled_bk;
+  g.raster_gb = plan->raster_gb;
+  g.zero_row = ws + L.off_zero;
+  const bool t8 = tg == kTgTiled && plan->tiled_bk == 0;
+  const int z2_gu = lora && t8 && fused_lora_ok(d, d.hidden);
+  const int z2_d = lora && t8 && fused_lora_ok(d, d.inter);
   g.topk_ids = ids;
   g.x = x;
   g.al = al;
@@ -387,6 +401,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     GemmArgs a = g;
     a.A = lora_a_gu;
     a.z_out = z_gu;
+    a.z2 = z2_gu;
     MOELORA_TRY(tg == kTgTiled && tiled_shrink_ok(d)
                     ? launch_tiled_shrink(a, false, st)
                     : launch_shrink(a, variant(d, tg, d.hidden, true), false, st));
@@ -397,6 +412,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.W = w_gate_up;
     a.B = lora_b_gu;
     a.z = z_gu;
+    a.z2 = z2_gu;
     a.waves = waves_gu;
     MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, true, vg, st) : launch_gate_up(a, vg, st));
   }
@@ -405,6 +421,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     GemmArgs a = g;
     a.A = lora_a_d;
     a.z_out = z_d;
+    a.z2 = z2_d;
     MOELORA_TRY(tg == kTgTiled && tiled_shrink_ok(d)
                     ? launch_tiled_shrink(a, true, st)
                     : launch_shrink(a, variant(d, tg, d.inter, true), true, st));
@@ -415,6 +432,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.W = w_down;
     a.B = lora_b_d;
     a.z = z_d;
+    a.z2 = z2_d;
     a.waves = waves_d;
     if (row) {
       a.rs = RowShrinkArgs{h, lora_a_d, z_d, adapter_ids, d.inter, vd.vec};

@@ -63,7 +63,11 @@ struct GemmArgs {
   RowShrinkArgs rs;        // row mode: the down shrink riding along with down
   int row_wgs;             // row mode: leading workgroups that run rs
   int waves;               // waves per workgroup of the GEMM kernels (16 columns each)
-  int tiled_bk;            // LDS-tiled kernels: contraction slab (32 or 64)
+  int raster_gb;           // 8-wave tiled GEMM: token blocks per workgroup raster group
+  int tiled_bk;            // tiled GEMM: 0 = 8-wave kernel where K % 64 == 0, else 4-wave slab (32 / 64)
+  int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
+                           // result (tiled shrink -> 8-wave GEMM); zero_row: 64 bf16 zeros
+  void *zero_row;
   void *h;                 // [cap][I] SiLU(gate)*up, layer dtype
   float *y;                // [R][H] down output per routed row
   AlignBufs al;

@@ -38,6 +38,125 @@ __device__ __forceinline__ void mma32(f32x16_t &c, u32x4_t a, u32x4_t b) {
                                               __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// LoRA expand (acc += B_rows . z^T for each LoRA tile of the block) and the
+// epilogue of a tiled workgroup: 128 tokens of block blk against TW weight
+// rows starting at output column n0 (gate_up: TW/2 gate rows then the
+// matching TW/2 up rows).  The wave owns weight-tile rows wt0 .. wt0+31 and
+// wt1 .. wt1+31 against the block's four 32-token tiles.
+template <bool GATE_UP, bool LORA, int TW>
+__device__ __forceinline__ void tile_finish(const GemmArgs &a, f32x16_t (&acc)[2][4], int blk, int e,
+                                            int n0, int wt0, int wt1, int li, int lh) {
+  const Shape &s = a.s;
+  const int I = s.I, H = s.H;
+  const int Nout = GATE_UP ? I : H;
+  // ---- LoRA expand: acc += B_rows . z^T for each LoRA tile of the block
+  if (LORA) {
+    const int r = s.r;
+    const uint16_t *Bm = static_cast<const uint16_t *>(a.B);
+    const int t0 = a.al.block_tile_start[blk], t1 = a.al.block_tile_start[blk + 1];
+    const size_t stride = (size_t)s.cap * r;
+    for (int ti = t0; ti < t1; ++ti) {
+      const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[ti];
+      const int ad = tl.y, lo = tl.z, n = tl.w;
+      const uint16_t *bw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int wr = (i == 0 ? wt0 : wt1) + li;
+        int row;
+        if (GATE_UP) row = (wr < TW / 2 ? 0 : I) + min(n0 + (wr & (TW / 2 - 1)), I - 1);
+        else row = min(n0 + wr, H - 1);
+        bw[i] = Bm + (((size_t)ad * s.E + e) * (GATE_UP ? 2 * I : H) + row) * r;
+      }
+      for (int kc = 0; kc < r; kc += 16) {
+        const int kk = kc + lh * 8;
+        const u32x4_t c0 = load_chunk_any<uint16_t, true>(bw[0], kk, r);
+        const u32x4_t c1 = load_chunk_any<uint16_t, true>(bw[1], kk, r);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int local = b * 32 + li;
+          float zv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) zv[q] = 0.f;
+          if (local >= lo && local < lo + n && kk < r) {
+            const float *zp = a.z + ((size_t)blk * kTM + local) * r + kk;
+            for (int sp = 0; sp < a.split; ++sp) {
+              const float4 v0 = *reinterpret_cast<const float4 *>(zp + sp * stride);
+              const float4 v1 = *reinterpret_cast<const float4 *>(zp + sp * stride + 4);
+              zv[0] += v0.x, zv[1] += v0.y, zv[2] += v0.z, zv[3] += v0.w;
+              zv[4] += v1.x, zv[5] += v1.y, zv[6] += v1.z, zv[7] += v1.w;
+            }
+          }
+          u32x4_t zh, zl;
+          SplitF32<uint16_t>::run(zv, zh, zl);
+          mma32(acc[0][b], c0, zh);
+          mma32(acc[0][b], c0, zl);
+          mma32(acc[1][b], c1, zh);
+          mma32(acc[1][b], c1, zl);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue.  Lane holds, for token tile b, token column 32 b + li and
+  // weight rows 8 (v / 4) + 4 lh + v % 4 of each of its two weight tiles.
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int pos = blk * kTM + b * 32 + li;
+    const int p = a.al.sorted_rows[pos];
+    if (p >= s.R) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int wr = 8 * g + 4 * lh;  // first of 4 consecutive rows in the wave's tile
+      if (GATE_UP) {
+        const int col = n0 + wt0 + wr;  // h column
+        uint16_t hv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          hv[v] = f32_to_bf16(silu_f32(acc[0][b][4 * g + v]) * acc[1][b][4 * g + v]);
+        uint16_t *dst = static_cast<uint16_t *>(a.h) + (size_t)pos * I + col;
+        if (col + 3 < Nout) {
+          *reinterpret_cast<uint2 *>(dst) = __builtin_bit_cast(uint2, hv);
+        } else {
+          for (int v = 0; v < 4; ++v)
+            if (col + v < Nout) dst[v] = hv[v];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int m = n0 + (i == 0 ? wt0 : wt1) + wr;
+          float *dst = a.y + (size_t)p * H + m;
+          if (m + 3 < Nout) {
+            *reinterpret_cast<float4 *>(dst) =
+                make_float4(acc[i][b][4 * g], acc[i][b][4 * g + 1], acc[i][b][4 * g + 2],
+                            acc[i][b][4 * g + 3]);
+          } else {
+            for (int v = 0; v < 4; ++v)
+              if (m + v < Nout) dst[v] = acc[i][b][4 * g + v];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Workgroup id -> (token block, weight tile).  Ids run through groups of gb
+// consecutive token blocks; inside a group the blocks vary fastest, then the
+// weight tile.  The workgroups resident together on one XCD then share both
+// token blocks and weight tiles in that XCD's L2.  gb <= 0: blocks fastest
+// over the whole grid.
+__device__ __forceinline__ void tile_of(int id, int nblk, int ntn, int gb, int &blk, int &nt) {
+  if (gb <= 0 || gb >= nblk) {
+    blk = id % nblk;
+    nt = id / nblk;
+    return;
+  }
+  const int gsize = gb * ntn;
+  const int g = id / gsize, rem = id % gsize;
+  const int g0 = g * gb, gn = min(gb, nblk - g0);
+  blk = g0 + rem % gn;
+  nt = rem / gn;
+}
+
 template <int BK>
 struct Lds {
   static constexpr int kCpr = BK / 8;                // 16-byte chunks per row
@@ -70,7 +189,6 @@ __global__ __launch_bounds__(kTThreads, BK == 32 ? 2 : 1) void k_tiled(GemmArgs 
   if (e < 0) return;
   const int I = s.I, H = s.H;
   const int K = GATE_UP ? H : I;
-  const int Nout = GATE_UP ? I : H;              // valid output columns of this projection
   const int n0 = nt * (GATE_UP ? kTW / 2 : kTW);  // first output column of the tile
 
   // ---- per-thread global load plan: thread t loads chunk (t % kCpr) of
@@ -180,94 +298,165 @@ __global__ __launch_bounds__(kTThreads, BK == 32 ? 2 : 1) void k_tiled(GemmArgs 
     __syncthreads();
   }
 
-  // ---- LoRA expand: acc += B_rows . z^T for each LoRA tile of the block
-  if (LORA) {
-    const int r = s.r;
-    const uint16_t *Bm = static_cast<const uint16_t *>(a.B);
-    const int t0 = a.al.block_tile_start[blk], t1 = a.al.block_tile_start[blk + 1];
-    const size_t stride = (size_t)s.cap * r;
-    for (int ti = t0; ti < t1; ++ti) {
-      const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[ti];
-      const int ad = tl.y, lo = tl.z, n = tl.w;
-      const uint16_t *bw[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int wr = (i == 0 ? wt0 : wt1) + li;
-        int row;
-        if (GATE_UP) row = (wr < kTW / 2 ? 0 : I) + min(n0 + (wr & (kTW / 2 - 1)), I - 1);
-        else row = min(n0 + wr, H - 1);
-        bw[i] = Bm + (((size_t)ad * s.E + e) * (GATE_UP ? 2 * I : H) + row) * r;
-      }
-      for (int kc = 0; kc < r; kc += 16) {
-        const int kk = kc + lh * 8;
-        const u32x4_t c0 = load_chunk_any<uint16_t, true>(bw[0], kk, r);
-        const u32x4_t c1 = load_chunk_any<uint16_t, true>(bw[1], kk, r);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int local = b * 32 + li;
-          float zv[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) zv[q] = 0.f;
-          if (local >= lo && local < lo + n && kk < r) {
-            const float *zp = a.z + ((size_t)blk * kTM + local) * r + kk;
-            for (int sp = 0; sp < a.split; ++sp) {
-              const float4 v0 = *reinterpret_cast<const float4 *>(zp + sp * stride);
-              const float4 v1 = *reinterpret_cast<const float4 *>(zp + sp * stride + 4);
-              zv[0] += v0.x, zv[1] += v0.y, zv[2] += v0.z, zv[3] += v0.w;
-              zv[4] += v1.x, zv[5] += v1.y, zv[6] += v1.z, zv[7] += v1.w;
-            }
-          }
-          u32x4_t zh, zl;
-          SplitF32<uint16_t>::run(zv, zh, zl);
-          mma32(acc[0][b], c0, zh);
-          mma32(acc[0][b], c0, zl);
-          mma32(acc[1][b], c1, zh);
-          mma32(acc[1][b], c1, zl);
-        }
-      }
-    }
-  }
+  tile_finish<GATE_UP, LORA, kTW>(a, acc, blk, e, n0, wt0, wt1, li, lh);
+}
 
-  // ---- epilogue.  Lane holds, for token tile b, token column 32 b + li and
-  // weight rows 8 (v / 4) + 4 lh + v % 4 of each of its two weight tiles.
+// 8-wave variant for contractions that are a multiple of 64: workgroup tile
+// 128 tokens x 512 weight rows, one workgroup per CU, two waves per SIMD.
+// Wave w owns weight rows 64w .. 64w+63 (gate_up: gate rows 32w .. +31 and
+// the matching up rows 256 + 32w .. +31) against all 128 tokens.
+//
+// Slabs are 64 contraction indices wide, so a weight or token row
+// contributes one whole 128-byte cache line per slab: each group of 8 lanes
+// fetches one line with global_load_lds_dwordx4, straight into LDS without
+// passing through registers, and every L2 request is a full line.  Two LDS
+// stages of 80 KB: the loads of slab s+1 go to one while the MFMAs of slab s
+// read the other; one barrier per slab.  A row's 16-byte chunk c sits at
+// chunk c ^ ((row / 2) % 8) of its 128-byte LDS row, which keeps the
+// fragment reads (32 rows at chunk c, 32 rows at chunk c ^ 1) free of bank
+// conflicts.
+constexpr int kT8Waves = 8;
+constexpr int kT8Threads = kT8Waves * kWave;
+constexpr int kT8W = 512;                                 // weight rows per tile
+constexpr int kT8Row = 128;                               // LDS bytes per row (64 bf16)
+constexpr int kT8Stage = (kT8W + kTM) * kT8Row;           // 80 KB
+constexpr int kT8Lds = 2 * kT8Stage;
+
+__device__ __forceinline__ int t8_off(int row, int c) { return row * kT8Row + ((c ^ ((row >> 1) & 7)) << 4); }
+
+template <bool GATE_UP, bool LORA>
+__global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Shape &s = a.s;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int li = lane & 31, lh = lane >> 5;
+
+  int blk, nt;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), s.nblk, gridDim.x / s.nblk, a.raster_gb, blk, nt);
+  const int e = a.al.block_expert[blk];
+  if (e < 0) return;
+  const int I = s.I, H = s.H;
+  const int K = GATE_UP ? H : I;
+  const int n0 = nt * (GATE_UP ? kT8W / 2 : kT8W);
+
+  // Load plan: LDS row group j (8 rows, 1 KB) is filled by one wave
+  // instruction, lane i bringing logical chunk (i % 8) ^ ((row / 2) % 8) of
+  // row 8j + i / 8 -- the chunk that t8_off places at byte 16 i of the group.
+  // Wave w fills weight groups 8w .. 8w+7 and token groups 64 + 2w, 65 + 2w.
+  const int lrow = lane >> 3;
+  const uint16_t *src[10];
+  {
+    const uint16_t *W = static_cast<const uint16_t *>(a.W);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int pos = blk * kTM + b * 32 + li;
-    const int p = a.al.sorted_rows[pos];
-    if (p >= s.R) continue;
+    for (int j = 0; j < 8; ++j) {
+      const int r = 64 * wave + 8 * j + lrow;  // weight-tile row
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      size_t row;
+      if (GATE_UP) row = (size_t)e * 2 * I + (r < kT8W / 2 ? 0 : I) + min(n0 + (r & (kT8W / 2 - 1)), I - 1);
+      else row = (size_t)e * H + min(n0 + r, H - 1);
+      src[j] = W + row * K + 8 * c;
+    }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int wr = 8 * g + 4 * lh;  // first of 4 consecutive rows in the wave's tile
-      if (GATE_UP) {
-        const int col = n0 + wt0 + wr;  // h column
-        uint16_t hv[4];
+    for (int j = 0; j < 2; ++j) {
+      const int t = 16 * wave + 8 * j + lrow;  // token row of the block
+      const int c = (lane & 7) ^ (((kT8W + t) >> 1) & 7);
+      const int pos = blk * kTM + t;
+      // padding rows read a valid row; their output columns are dropped
+      const int p = a.al.sorted_rows[pos];
+      const uint16_t *row;
+      if (GATE_UP) row = static_cast<const uint16_t *>(a.x) + (size_t)(p < s.R ? p / s.k : 0) * H;
+      else row = static_cast<const uint16_t *>(a.h) + (size_t)(p < s.R ? pos : blk * kTM) * I;
+      src[8 + j] = row + 8 * c;
+    }
+  }
+  const int nbase = K / 64;
+  // LoRA expand as extra slabs: for LoRA tile (adapter ad, block rows
+  // lo .. lo+n-1) the contraction runs over the 2r entries (z hi | z lo) of
+  // each token against (B row | B row) of each weight row; tokens outside
+  // the tile's run read zeros.
+  int t0 = 0, nlt = 0;
+  if (LORA) {
+    t0 = a.al.block_tile_start[blk];
+    nlt = a.al.block_tile_start[blk + 1] - t0;
+  }
+  const int lsl = LORA ? s.r / 32 : 0;  // slabs per LoRA tile
+  const int nks = nbase + nlt * lsl;
+
+  auto dma = [&](const uint16_t *g, unsigned char *l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+  };
+  auto issue = [&](int ks, int buf) {
+    unsigned char *st = smem + buf * kT8Stage;
+    if (!LORA || ks < nbase) {
+      const int k = ks * 64;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          hv[v] = f32_to_bf16(silu_f32(acc[0][b][4 * g + v]) * acc[1][b][4 * g + v]);
-        uint16_t *dst = static_cast<uint16_t *>(a.h) + (size_t)pos * I + col;
-        if (col + 3 < Nout) {
-          *reinterpret_cast<uint2 *>(dst) = __builtin_bit_cast(uint2, hv);
-        } else {
-          for (int v = 0; v < 4; ++v)
-            if (col + v < Nout) dst[v] = hv[v];
-        }
-      } else {
+      for (int j = 0; j < 8; ++j) dma(src[j] + k, st + (64 * wave + 8 * j) * kT8Row);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int m = n0 + (i == 0 ? wt0 : wt1) + wr;
-          float *dst = a.y + (size_t)p * H + m;
-          if (m + 3 < Nout) {
-            *reinterpret_cast<float4 *>(dst) =
-                make_float4(acc[i][b][4 * g], acc[i][b][4 * g + 1], acc[i][b][4 * g + 2],
-                            acc[i][b][4 * g + 3]);
-          } else {
-            for (int v = 0; v < 4; ++v)
-              if (m + v < Nout) dst[v] = acc[i][b][4 * g + v];
-          }
-        }
+      for (int j = 0; j < 2; ++j) dma(src[8 + j] + k, st + (kT8W + 16 * wave + 8 * j) * kT8Row);
+      return;
+    }
+    const int u = ks - nbase, q = u % lsl;
+    const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[t0 + u / lsl];
+    const int ad = tl.y, lo = tl.z, n = tl.w, r = s.r, rc = r / 8;
+    const uint16_t *Bm = static_cast<const uint16_t *>(a.B) +
+                         ((size_t)ad * s.E + e) * (size_t)(GATE_UP ? 2 * I : H) * r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rr = 64 * wave + 8 * j + lrow;
+      const int kc = 8 * q + ((lane & 7) ^ ((rr >> 1) & 7));  // chunk of (hi | lo)
+      int row;
+      if (GATE_UP) row = (rr < kT8W / 2 ? 0 : I) + min(n0 + (rr & (kT8W / 2 - 1)), I - 1);
+      else row = min(n0 + rr, H - 1);
+      dma(Bm + (size_t)row * r + 8 * (kc % rc), st + (64 * wave + 8 * j) * kT8Row);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = 16 * wave + 8 * j + lrow;
+      const int c = (lane & 7) ^ ((t >> 1) & 7);
+      const uint16_t *zs = (t >= lo && t < lo + n)
+                               ? static_cast<const uint16_t *>(static_cast<const void *>(a.z)) +
+                                     ((size_t)blk * kTM + t) * 2 * r + 64 * q + 8 * c
+                               : static_cast<const uint16_t *>(a.zero_row) + 8 * c;
+      dma(zs, st + (kT8W + 16 * wave + 8 * j) * kT8Row);
+    }
+  };
+
+  const int wt0 = GATE_UP ? wave * 32 : wave * 64;
+  const int wt1 = GATE_UP ? kT8W / 2 + wave * 32 : wave * 64 + 32;
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[i][b] = f32x16_t{};
+
+  issue(0, 0);
+  for (int ks = 0; ks < nks; ++ks) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of slab ks are in LDS
+    __syncthreads();                     // ... and every wave's; slab ks - 1 fully consumed
+    if (ks + 1 < nks) issue(ks + 1, (ks + 1) & 1);
+    const unsigned char *st = smem + (ks & 1) * kT8Stage;
+    u32x4_t fa[2][2], fb[2][4];
+    auto fread = [&](int kk, int slot) {
+      const int c = 2 * kk + lh;
+      fa[slot][0] = *reinterpret_cast<const u32x4_t *>(st + t8_off(wt0 + li, c));
+      fa[slot][1] = *reinterpret_cast<const u32x4_t *>(st + t8_off(wt1 + li, c));
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        fb[slot][b] = *reinterpret_cast<const u32x4_t *>(st + t8_off(kT8W + b * 32 + li, c));
+    };
+    fread(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) fread(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        mma32(acc[0][b], fa[kk & 1][0], fb[kk & 1][b]);
+        mma32(acc[1][b], fa[kk & 1][1], fb[kk & 1][b]);
       }
     }
   }
+  tile_finish<GATE_UP, false, kT8W>(a, acc, blk, e, n0, wt0, wt1, li, lh);
 }
 
 // LoRA shrink for 128-row blocks: z[pos][c] = X[pos] . A[a][e][c] for the
@@ -361,6 +550,31 @@ __global__ __launch_bounds__(kTThreads) void k_tiled_shrink(GemmArgs a) {
   }
   // lane: token column wave*32 + li; A rows 32 i + 8 (v/4) + 4 lh + v%4
   const int local = wave * 32 + li;
+  if (a.z2) {
+    // bf16 rows (hi | lo): hi = bf16(z), lo = bf16(z - hi); the first tile
+    // also clears the zero row that masked expand lanes read
+    if (tile == 0 && tid < 8)
+      reinterpret_cast<u32x4_t *>(a.zero_row)[tid] = u32x4_t{0, 0, 0, 0};
+    if (local < lo || local >= lo + n) return;
+    uint16_t *zrow = reinterpret_cast<uint16_t *>(a.z_out) + ((size_t)blk * kTM + local) * 2 * r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * i + 8 * g + 4 * lh;
+        if (c >= r) continue;  // r is a multiple of 32 here
+        uint16_t hi[4], lo4[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float zv = acc[i][4 * g + v];
+          hi[v] = f32_to_bf16(zv);
+          lo4[v] = f32_to_bf16(zv - bf16_to_f32(hi[v]));
+        }
+        *reinterpret_cast<uint2 *>(zrow + c) = __builtin_bit_cast(uint2, hi);
+        *reinterpret_cast<uint2 *>(zrow + r + c) = __builtin_bit_cast(uint2, lo4);
+      }
+    return;
+  }
   if (local < lo || local >= lo + n) return;
   float *zrow = a.z_out + ((size_t)blk * kTM + local) * r;
 #pragma unroll
@@ -388,6 +602,18 @@ hipError_t go_tiled(const GemmArgs &a, hipStream_t st) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(kern, dim3(ntn * a.s.nblk), dim3(kTThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <bool GATE_UP, bool LORA>
+hipError_t go_tiled8(const GemmArgs &a, hipStream_t st) {
+  const int cols = GATE_UP ? kT8W / 2 : kT8W;
+  const int ntn = ((GATE_UP ? a.s.I : a.s.H) + cols - 1) / cols;
+  auto kern = k_tiled8<GATE_UP, LORA>;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kT8Lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(kern, dim3(ntn * a.s.nblk), dim3(kT8Threads), kT8Lds, st, a);
   return hipGetLastError();
 }
 
@@ -419,6 +645,9 @@ hipError_t launch_tiled(const GemmArgs &a, bool gate_up, const GemmVariant &v, h
   if (a.s.nblk == 0) return hipSuccess;
   if (!v.bf16 || !v.vec || a.s.BM != kTM) return hipErrorInvalidValue;
   const int K = gate_up ? a.s.H : a.s.I;
+  if (a.tiled_bk == 0 && K % 64 == 0 && (!v.lora || a.z2))
+    return gate_up ? (v.lora ? go_tiled8<true, true>(a, st) : go_tiled8<true, false>(a, st))
+                   : (v.lora ? go_tiled8<false, true>(a, st) : go_tiled8<false, false>(a, st));
   const int bk = a.tiled_bk == 64 ? 64 : 32;
   const bool even_k = K % bk == 0;
   if (bk == 64)

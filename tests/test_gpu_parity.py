@@ -49,6 +49,8 @@ SMALL = [
     (300, 256, 320, 4, 2, 3, 16, "bf16", "uniform_with_none"),  # LDS-tiled, partial column tile
     (260, 200, 136, 4, 2, 2, 32, "bf16", "uniform_with_none"),  # LDS-tiled, K % 64 != 0
     (512, 128, 128, 2, 1, 0, 0, "bf16", "none"),                # LDS-tiled, no adapters
+    (300, 256, 192, 4, 2, 3, 32, "bf16", "uniform_with_none"),  # 8-wave tiled, LoRA slabs (2r = 64)
+    (400, 128, 256, 2, 2, 5, 64, "bf16", "uniform_with_none"),  # 8-wave tiled, several LoRA tiles per block
 ]
 
 
