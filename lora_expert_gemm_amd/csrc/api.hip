@@ -42,14 +42,14 @@ struct moelora_plan_s {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kTgSmall = 1, kTgLarge = 4, kTgTiled = 8;
+constexpr int kTgSmall = 1, kTgMid = 2, kTgLarge = 4, kTgTiled = 8;
 
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-// Token-count bucket: blocks of 16 rows while an expert gets about one
-// block of rows (weight streaming), blocks of 128 rows for the LDS-tiled
-// MFMA kernels once experts average 64 rows or more (bf16 with 16-byte
-// aligned rows), else blocks of 64.
+// Token-count bucket (block of 16 * tg rows): weight-streaming blocks of 16,
+// 32 or 64 rows sized to hold an expert's rows in one block, blocks of 128
+// rows for the LDS-tiled MFMA kernels once experts average 64 rows or more
+// (bf16 with 16-byte aligned rows).
 bool tiled_ok(const moelora_desc &d) {
   return d.dtype == MOELORA_BF16 && d.hidden % 8 == 0 && d.inter % 8 == 0 && d.rank % 8 == 0;
 }
@@ -61,16 +61,28 @@ bool fused_lora_ok(const moelora_desc &d, int K) {
 }
 int choose_tg(const moelora_desc &d, int T) {
   const long long rows = (long long)T * d.top_k;
-  if (rows <= 24LL * d.n_experts) return kTgSmall;
-  if (tiled_ok(d) && rows >= 64LL * d.n_experts) return kTgTiled;
+  const long long ne = std::max<long long>(1, std::min<long long>(d.n_experts, rows));
+  // Streaming blocks: 16 rows while experts average at most 4 rows, then 32
+  // rows (most experts' rows in one block, so their weights stream once,
+  // without the register cost of 64-row blocks).
+  if (tiled_ok(d) && rows >= 64 * ne) return kTgTiled;
+  // tuning sweeps only: force the streaming block size (1, 2 or 4 groups of 16)
+  if (const char *v = getenv("MOELORA_TG")) {
+    const int tg = atoi(v);
+    if (tg == 1 || tg == 2 || tg == 4) return tg;
+  }
+  if (rows <= 4 * ne) return kTgSmall;
+  if (rows <= 32 * ne) return kTgMid;
   return kTgLarge;
 }
 
 // Waves (16 output columns each) per GEMM workgroup.  The decode weight
 // stream wants thousands of small workgroups: 64 weight rows per workgroup
-// (gate_up: 2 waves x (16 gate + 16 up) rows; down: 4 waves x 16 rows).
+// (gate_up: 2 waves x (16 gate + 16 up) rows; down: 4 waves x 16 rows); the
+// same for 32-row blocks (measured best over 1, 2, 4 waves on both
+// medium-batch shapes within a few percent).
 int choose_waves(int tg, bool gate_up) {
-  if (tg == kTgSmall) return gate_up ? 2 : 4;
+  if (tg <= kTgMid) return gate_up ? 2 : 4;
   return 4;
 }
 
@@ -182,7 +194,7 @@ GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora, bool rowz =
 // into the combine.  Needs the one-workgroup alignment and down workgroups
 // with at least r (rounded up to a power of two) threads.
 bool use_row_mode(const Shape &s, bool lora, int waves_d) {
-  if (!lora || s.R > kSmallRows || s.BM != 16) return false;
+  if (!lora || s.R > kSmallRows || s.BM > 64) return false;
   int rp = 1;
   while (rp < s.r) rp <<= 1;
   return 64 * waves_d >= rp;  // 64 threads per wave

@@ -47,7 +47,7 @@ __device__ __forceinline__ u32x4_t ld(const DT *row, int k, int len) {
 // Token rows with ok false contribute zeros.
 template <typename DT, int TG, int U, bool VEC, bool EVEN_K, bool TWO>
 __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *const *xr,
-                                         const bool *ok, int K, int kg, f32x4_t *acc0,
+                                         const bool *ok, int ntg, int K, int kg, f32x4_t *acc0,
                                          f32x4_t *acc1) {
   using M = Mma<DT>;
   constexpr int EPC = Elem<DT>::kPerChunk;
@@ -63,12 +63,13 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
       if (TWO) a1[u] = ld<DT, VEC>(w1, k, K);
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg)
-        b[u][tg] = ok[tg] ? ld<DT, VEC>(xr[tg], k, K) : u32x4_t{0, 0, 0, 0};
+        if (tg < ntg) b[u][tg] = ok[tg] ? ld<DT, VEC>(xr[tg], k, K) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) {
+        if (tg >= ntg) continue;
         M::step(acc0[tg], a0[u], b[u][tg]);
         if (TWO) M::step(acc1[tg], a1[u], b[u][tg]);
       }
@@ -79,6 +80,7 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
     const u32x4_t a1 = TWO ? ld<DT, VEC>(w1, k, K) : a0;
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
+      if (tg >= ntg) continue;
       const u32x4_t b = ok[tg] ? ld<DT, VEC>(xr[tg], k, K) : u32x4_t{0, 0, 0, 0};
       M::step(acc0[tg], a0, b);
       if (TWO) M::step(acc1[tg], a1, b);
@@ -90,6 +92,7 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
     const u32x4_t a1 = TWO ? load_chunk_any<DT, VEC>(w1, k, K) : a0;
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) {
+      if (tg >= ntg) continue;
       const u32x4_t b = ok[tg] ? load_chunk_any<DT, VEC>(xr[tg], k, K) : u32x4_t{0, 0, 0, 0};
       M::step(acc0[tg], a0, b);
       if (TWO) M::step(acc1[tg], a1, b);
@@ -166,6 +169,18 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, const 
   }
 }
 
+// Token groups (16 rows) of block blk that hold a routed row.  An expert's
+// rows fill its blocks from the front and padding sits at the end of its
+// last block, so these are the leading groups; the rest are skipped.
+template <int TG>
+__device__ __forceinline__ int active_groups(const GemmArgs &a, int blk) {
+  int n = 0;
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+    if (a.al.sorted_rows[blk * 16 * TG + tg * 16] < a.s.R) n = tg + 1;
+  return n;
+}
+
 // Workgroup -> (block, column tile).  Consecutive logical ids walk the
 // blocks of one column tile, so the blocks of one expert share an XCD.
 struct GemmTile {
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
     ag[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     au[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, ok, H, kg, ag, au);
+  contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, ok, active_groups<TG>(a, blk), H, kg, ag, au);
   if (MODE != 0)
     expand<DT, TG, VEC, true, MODE == 2>(a, blk, e, static_cast<const DT *>(a.B), (size_t)2 * I,
                                          nrow, (size_t)I, kg, ri, prow, ag, au);
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   f32x4_t acc[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  contract<DT, TG, U, VEC, EVEN_K, false>(wd, wd, xr, ok, I, kg, acc, acc);
+  contract<DT, TG, U, VEC, EVEN_K, false>(wd, wd, xr, ok, active_groups<TG>(a, blk), I, kg, acc, acc);
   if (MODE == 1)
     expand<DT, TG, VEC, false, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow, 0,
                                       kg, ri, prow, acc, acc);
@@ -484,15 +499,18 @@ __global__ __launch_bounds__(64) void k_combine_rows(Shape s, const int *__restr
 
 // ------------------------------------------------------------- dispatch
 
-// K-loop unroll: deep for 16-row blocks (weight streaming), shallower for
-// 64-row blocks (more accumulators).
-template <int TG> constexpr int unroll_for() { return TG == 1 ? 8 : 4; }
+// K-loop unroll (contraction steps in flight): 8 for 16-row blocks and for
+// the 32-row gate_up (two weight streams), else 4 (register pressure: the
+// 32-row down at 8 would drop to 3 waves per SIMD).
+template <int TG, bool GATE_UP> constexpr int unroll_for() {
+  return TG == 1 || (TG == 2 && GATE_UP) ? 8 : 4;
+}
 
 template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
   const int cols = 16 * a.waves;
   const int ntn = (a.s.I + cols - 1) / cols;
-  hipLaunchKernelGGL((k_gate_up<DT, TG, unroll_for<TG>(), VEC, EK, MODE>),
+  hipLaunchKernelGGL((k_gate_up<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE>),
                      dim3(ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
   return hipGetLastError();
 }
@@ -501,7 +519,7 @@ hipError_t go_down(const GemmArgs &a, hipStream_t st) {
   const int cols = 16 * a.waves;
   const int ntn = (a.s.H + cols - 1) / cols;
   const int extra = MODE == 2 ? a.row_wgs : 0;
-  hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG>(), VEC, EK, MODE>),
+  hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG, false>(), VEC, EK, MODE>),
                      dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
   return hipGetLastError();
 }
@@ -517,25 +535,19 @@ hipError_t go_shrink(const GemmArgs &a, hipStream_t st) {
   ((V).vec ? ((V).even_k ? GO<DT, TG, true, true, M>(a, st) : GO<DT, TG, true, false, M>(a, st)) \
            : GO<DT, TG, false, false, M>(a, st))
 
-// LoRA mode: 0 none, 1 tile-wise, 2 row-wise (16-row blocks only).
+// LoRA mode: 0 none, 1 tile-wise, 2 row-wise.
+#define MOELORA_MODES(GO, DT, TG, V)                                                 \
+  (mode == 0 ? MOELORA_VEK(GO, DT, TG, V, 0)                                         \
+   : mode == 1 ? MOELORA_VEK(GO, DT, TG, V, 1) : MOELORA_VEK(GO, DT, TG, V, 2))
 #define MOELORA_GEMM(GO, V)                                                          \
   do {                                                                               \
     const int mode = !(V).lora ? 0 : (V).rowz ? 2 : 1;                                \
-    if (mode == 2 && (V).tg != 1) return hipErrorInvalidValue;                       \
-    if ((V).tg == 1) {                                                               \
-      if ((V).bf16)                                                                  \
-        return mode == 0 ? MOELORA_VEK(GO, uint16_t, 1, V, 0)                        \
-             : mode == 1 ? MOELORA_VEK(GO, uint16_t, 1, V, 1)                        \
-                         : MOELORA_VEK(GO, uint16_t, 1, V, 2);                       \
-      return mode == 0 ? MOELORA_VEK(GO, float, 1, V, 0)                             \
-           : mode == 1 ? MOELORA_VEK(GO, float, 1, V, 1)                             \
-                       : MOELORA_VEK(GO, float, 1, V, 2);                            \
-    }                                                                                \
-    if ((V).tg == 4) {                                                               \
-      if ((V).bf16)                                                                  \
-        return mode == 0 ? MOELORA_VEK(GO, uint16_t, 4, V, 0) : MOELORA_VEK(GO, uint16_t, 4, V, 1); \
-      return mode == 0 ? MOELORA_VEK(GO, float, 4, V, 0) : MOELORA_VEK(GO, float, 4, V, 1); \
-    }                                                                                \
+    if ((V).tg == 1)                                                                 \
+      return (V).bf16 ? MOELORA_MODES(GO, uint16_t, 1, V) : MOELORA_MODES(GO, float, 1, V); \
+    if ((V).tg == 2)                                                                 \
+      return (V).bf16 ? MOELORA_MODES(GO, uint16_t, 2, V) : MOELORA_MODES(GO, float, 2, V); \
+    if ((V).tg == 4)                                                                 \
+      return (V).bf16 ? MOELORA_MODES(GO, uint16_t, 4, V) : MOELORA_MODES(GO, float, 4, V); \
     return hipErrorInvalidValue;                                                     \
   } while (0)
 
@@ -544,6 +556,9 @@ hipError_t go_shrink(const GemmArgs &a, hipStream_t st) {
     if ((V).tg == 1)                                                                 \
       return (V).bf16 ? MOELORA_VEK(go_shrink, uint16_t, 1, V, FH)                   \
                       : MOELORA_VEK(go_shrink, float, 1, V, FH);                     \
+    if ((V).tg == 2)                                                                 \
+      return (V).bf16 ? MOELORA_VEK(go_shrink, uint16_t, 2, V, FH)                   \
+                      : MOELORA_VEK(go_shrink, float, 2, V, FH);                     \
     if ((V).tg == 4)                                                                 \
       return (V).bf16 ? MOELORA_VEK(go_shrink, uint16_t, 4, V, FH)                   \
                       : MOELORA_VEK(go_shrink, float, 4, V, FH);                     \

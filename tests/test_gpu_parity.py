@@ -51,6 +51,9 @@ SMALL = [
     (512, 128, 128, 2, 1, 0, 0, "bf16", "none"),                # LDS-tiled, no adapters
     (300, 256, 192, 4, 2, 3, 32, "bf16", "uniform_with_none"),  # 8-wave tiled, LoRA slabs (2r = 64)
     (400, 128, 256, 2, 2, 5, 64, "bf16", "uniform_with_none"),  # 8-wave tiled, several LoRA tiles per block
+    (30, 128, 96, 8, 2, 3, 16, "bf16", "uniform_with_none"),    # 32-row blocks, row-wise LoRA
+    (200, 128, 96, 64, 2, 3, 16, "bf16", "uniform_with_none"),  # 32-row blocks, tile-wise LoRA
+    (60, 256, 128, 8, 2, 4, 16, "bf16", "uniform_with_none"),   # 64-row blocks, row-wise LoRA
 ]
 
 
