@@ -64,10 +64,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/hbm_traffic.json), or None when there is none for this
-    workload or the kernel sources changed since the counters were taken."""
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of the kernel that ran `stage` (e.g. "gate_up")
+    from the committed rocprofv3 counter summary (profiles/hbm_traffic.json),
+    or None when there is none for this workload or the kernel sources
+    changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -75,10 +76,8 @@ def measured_traffic(workload, kernel):
         t = json.load(f)
     if t.get("kernel_source") != kernel_source_hash():
         return None
-    for name, v in t.get("workloads", {}).get(workload, {}).items():
-        if name.startswith("k_" + kernel + "<"):
-            return v["bytes"]
-    return None
+    v = t.get("workloads", {}).get(workload, {}).get(stage)
+    return v["bytes"] if v else None
 
 
 def algorithmic(w, ids, aid):

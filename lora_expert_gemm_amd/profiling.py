@@ -1,0 +1,165 @@
+"""Summaries of rocprofv3 output for the layer's kernels.
+
+Turns the CSV files of two kinds of rocprofv3 runs into the short text
+summaries kept under ``profiles/``:
+
+* ``--kernel-trace --stats``: average duration and share of each kernel
+  (``<name>_kernel_stats.csv``);
+* ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (one counter per run):
+  HBM bytes per dispatch, scaled by what the same counters report for a
+  plain device copy of known size (``<name>_counter_collection.csv``).
+
+Kernels are keyed by the pipeline stage they implement, so a reader (such as
+bench.py's roofline) can find the bytes of "gate_up" whichever kernel
+variant ran it.
+
+Usage::
+
+    python -m lora_expert_gemm_amd.profiling stats <workload> <stats.csv> <out.md> <command...>
+    python -m lora_expert_gemm_amd.profiling traffic <workload> <fetch.csv> <write.csv> \
+        <copy_fetch.csv> <copy_write.csv> <copy_mib> <traffic.json> <out.md> <source_hash> <command...>
+
+The trailing words are the rocprofv3 command(s) that made the CSVs, recorded
+in the summary; a ";;" word separates commands.
+"""
+import csv
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+# kernel name prefix -> pipeline stage (first match wins)
+_STAGES = [
+    ("k_route_align_small", "route_align"),
+    ("k_route", "route_align"),
+    ("k_align", "route_align"),
+    ("k_tiled_shrink<false", "shrink_gate_up"),
+    ("k_tiled_shrink<true", "shrink_down"),
+    ("k_shrink<", None),  # resolved from the FROM_H template argument below
+    ("k_tiled8<true", "gate_up"),
+    ("k_tiled8<false", "down"),
+    ("k_tiled<true", "gate_up"),
+    ("k_tiled<false", "down"),
+    ("k_gate_up", "gate_up"),
+    ("k_down", "down"),
+    ("k_combine", "combine"),
+]
+
+
+def short_name(name):
+    """'void moelora::(anonymous namespace)::k_x<a, b>(moelora::GemmArgs)' -> 'k_x<a, b>'."""
+    m = re.search(r"(k_[a-z_0-9]+(<[^()]*>)?)", name)
+    return m.group(1) if m else name.strip()
+
+
+def stage_of(kernel):
+    k = short_name(kernel)
+    for prefix, stage in _STAGES:
+        if k.startswith(prefix):
+            if stage is None:  # k_shrink<DT, TG, VEC, EVEN_K, FROM_H>
+                return "shrink_down" if k.rstrip(">").split(",")[-1].strip() == "true" \
+                    else "shrink_gate_up"
+            return stage
+    return None
+
+
+def read_stats(path):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append(dict(kernel=short_name(r["Name"]), calls=int(r["Calls"]),
+                             avg_us=float(r["AverageNs"]) / 1e3, share=float(r["Percentage"])))
+    return rows
+
+
+def read_counter(path, counter):
+    """Mean value of `counter` per dispatch, per kernel (short name)."""
+    tot, n = defaultdict(float), defaultdict(int)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            k = short_name(r["Kernel_Name"])
+            tot[k] += float(r["Counter_Value"])
+            n[k] += 1
+    return {k: tot[k] / n[k] for k in tot}, dict(n)
+
+
+def write_stats_md(workload, stats_csv, out_md, command):
+    rows = read_stats(stats_csv)
+    lines = [f"# Kernel durations: {workload}", "",
+             "Command (run from /tmp with TMPDIR=/tmp):", "", "```", command, "```", "",
+             "| kernel | stage | calls | average (us) | share |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['kernel']} | {stage_of(r['kernel']) or '-'} | {r['calls']} | "
+                     f"{r['avg_us']:.2f} | {r['share']:.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rows
+
+
+def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib,
+                  traffic_json, out_md, source_hash, command):
+    fetch, nf = read_counter(fetch_csv, "FETCH_SIZE")
+    write, _ = read_counter(write_csv, "WRITE_SIZE")
+    cf, _ = read_counter(copy_fetch_csv, "FETCH_SIZE")
+    cw, _ = read_counter(copy_write_csv, "WRITE_SIZE")
+    kib = copy_mib * 1024.0
+    copy_kernel = max(cf, key=cf.get)  # the copy dominates its run
+    fs, ws = kib / cf[copy_kernel], kib / cw[copy_kernel]
+    entry = {}  # stage -> summed over the kernels that make up the stage
+    for k in fetch:
+        st = stage_of(k)
+        if st is None:
+            continue
+        b = (fetch[k] * fs + write.get(k, 0.0) * ws) * 1024.0
+        e = entry.setdefault(st, dict(kernel="", fetch_kib=0.0, write_kib=0.0, bytes=0.0))
+        e["kernel"] = (e["kernel"] + " + " if e["kernel"] else "") + k
+        e["fetch_kib"] += fetch[k]
+        e["write_kib"] += write.get(k, 0.0)
+        e["bytes"] += b
+    t = {}
+    if os.path.exists(traffic_json):
+        with open(traffic_json) as f:
+            t = json.load(f)
+    if t.get("kernel_source") != source_hash:
+        t = {"kernel_source": source_hash, "workloads": {}}
+    t["fetch_scale"], t["write_scale"] = fs, ws
+    t["workloads"][workload] = entry
+    with open(traffic_json, "w") as f:
+        json.dump(t, f, indent=1)
+    lines = [f"# HBM traffic counters: {workload}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; one counter per pass):", "", "```",
+             command, "```", "",
+             f"Kernel sources: `{source_hash}` (sha256 prefix over the device-kernel sources, "
+             "as bench.py computes it).", "",
+             f"Calibration: a plain {copy_mib} MiB device copy ({copy_kernel}) reports "
+             f"FETCH_SIZE = {cf[copy_kernel]:.0f} KiB and WRITE_SIZE = {cw[copy_kernel]:.0f} KiB "
+             f"per dispatch, so FETCH_SIZE is scaled by {fs:.4f} and WRITE_SIZE by {ws:.4f}.", "",
+             "| stage | kernel | dispatches | FETCH_SIZE (KiB, mean) | WRITE_SIZE (KiB, mean) "
+             "| scaled HBM bytes / launch |", "|---|---|---|---|---|---|"]
+    for st, v in entry.items():
+        disp = nf.get(v["kernel"].split(" + ")[0], 0)
+        lines.append(f"| {st} | {v['kernel']} | {disp} | {v['fetch_kib']:.0f} "
+                     f"| {v['write_kib']:.0f} | {v['bytes'] / 1e6:.1f} MB |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return entry
+
+
+def main(argv):
+    # command words; a ";;" word starts a new command line
+    def cmd(words):
+        return " ".join(words).replace(" ;; ", "\n")
+    if argv[0] == "stats":
+        write_stats_md(argv[1], argv[2], argv[3], cmd(argv[4:]))
+    elif argv[0] == "traffic":
+        (wl, fcsv, wcsv, cfcsv, cwcsv, mib, tj, md, h), rest = argv[1:10], argv[10:]
+        write_traffic(wl, fcsv, wcsv, cfcsv, cwcsv, float(mib), tj, md, h, cmd(rest))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
