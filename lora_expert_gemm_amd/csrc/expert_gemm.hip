@@ -45,43 +45,65 @@ __device__ __forceinline__ u32x4_t ld(const DT *row, int k, int len) {
 // acc[tg] += W_rows . X_rows^T over the contraction [0, K) for one or two
 // weight row pointers (TWO: gate and up), U steps of loads in flight.
 // Token rows with ok false contribute zeros.
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, bool TWO>
-__device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *const *xr,
-                                         const bool *ok, int ntg, int K, int kg, f32x4_t *acc0,
-                                         f32x4_t *acc1) {
+// acc[tg] += W_rows . X_rows^T over the whole contraction for NG token
+// groups.  Branch-free: every lane loads its operands unconditionally (a
+// padding row's x pointer aims at a valid row and its output column is never
+// written), which keeps the compiler's load counters exact so the two
+// register sets below really overlap.
+template <typename DT, int NG, int U, bool VEC, bool EVEN_K, bool TWO>
+__device__ __forceinline__ void contract_groups(const DT *w0, const DT *w1, const DT *const *xr,
+                                                int K, int kg, f32x4_t *acc0, f32x4_t *acc1) {
   using M = Mma<DT>;
   constexpr int EPC = Elem<DT>::kPerChunk;
   constexpr int KS = M::kK;
   const int nfull = K / KS;
-  int st = 0;
-  for (; st + U <= nfull; st += U) {
-    u32x4_t a0[U], a1[U], b[U][TG];
+  // Groups of U contraction steps in two register sets: the loads of group
+  // g + 1 are issued before the MFMAs of group g, so the weight stream never
+  // drains while a group waits for its slowest load.
+  struct Group {
+    u32x4_t a0[U], a1[U], b[U][NG];
+  };
+  auto load = [&](Group &g, int grp) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = (st + u) * KS + kg * EPC;
-      a0[u] = ld<DT, VEC>(w0, k, K);
-      if (TWO) a1[u] = ld<DT, VEC>(w1, k, K);
+      const int k = (grp * U + u) * KS + kg * EPC;
+      g.a0[u] = ld<DT, VEC>(w0, k, K);
+      if (TWO) g.a1[u] = ld<DT, VEC>(w1, k, K);
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg)
-        if (tg < ntg) b[u][tg] = ok[tg] ? ld<DT, VEC>(xr[tg], k, K) : u32x4_t{0, 0, 0, 0};
+      for (int tg = 0; tg < NG; ++tg) g.b[u][tg] = ld<DT, VEC>(xr[tg], k, K);
     }
+  };
+  auto compute = [&](const Group &g) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int tg = 0; tg < TG; ++tg) {
-        if (tg >= ntg) continue;
-        M::step(acc0[tg], a0[u], b[u][tg]);
-        if (TWO) M::step(acc1[tg], a1[u], b[u][tg]);
+      for (int tg = 0; tg < NG; ++tg) {
+        M::step(acc0[tg], g.a0[u], g.b[u][tg]);
+        if (TWO) M::step(acc1[tg], g.a1[u], g.b[u][tg]);
       }
+  };
+  const int ngroups = nfull / U;
+  Group ga, gb;
+  if (ngroups > 0) load(ga, 0);
+  // The loop body issues its loads unconditionally (the last pass reloads
+  // the final group, an L2 hit): a conditional load would leave the
+  // compiler unsure how many younger loads are outstanding, and it would
+  // then wait for all of them before the current group's MFMAs.
+  int grp = 0;
+  for (; grp + 2 <= ngroups; grp += 2) {
+    load(gb, grp + 1);
+    compute(ga);
+    load(ga, min(grp + 2, ngroups - 1));
+    compute(gb);
   }
-  for (; st < nfull; ++st) {
+  if (grp < ngroups) compute(ga);  // odd group count: the last one is in ga
+  for (int st = ngroups * U; st < nfull; ++st) {
     const int k = st * KS + kg * EPC;
     const u32x4_t a0 = ld<DT, VEC>(w0, k, K);
     const u32x4_t a1 = TWO ? ld<DT, VEC>(w1, k, K) : a0;
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      if (tg >= ntg) continue;
-      const u32x4_t b = ok[tg] ? ld<DT, VEC>(xr[tg], k, K) : u32x4_t{0, 0, 0, 0};
+    for (int tg = 0; tg < NG; ++tg) {
+      const u32x4_t b = ld<DT, VEC>(xr[tg], k, K);
       M::step(acc0[tg], a0, b);
       if (TWO) M::step(acc1[tg], a1, b);
     }
@@ -91,13 +113,25 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
     const u32x4_t a0 = load_chunk_any<DT, VEC>(w0, k, K);
     const u32x4_t a1 = TWO ? load_chunk_any<DT, VEC>(w1, k, K) : a0;
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-      if (tg >= ntg) continue;
-      const u32x4_t b = ok[tg] ? load_chunk_any<DT, VEC>(xr[tg], k, K) : u32x4_t{0, 0, 0, 0};
+    for (int tg = 0; tg < NG; ++tg) {
+      const u32x4_t b = load_chunk_any<DT, VEC>(xr[tg], k, K);
       M::step(acc0[tg], a0, b);
       if (TWO) M::step(acc1[tg], a1, b);
     }
   }
+}
+
+// The block's contraction over its ntg leading token groups (the rest hold
+// only padding and are skipped): one branch-free instance per group count.
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, bool TWO>
+__device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *const *xr, int ntg,
+                                         int K, int kg, f32x4_t *acc0, f32x4_t *acc1) {
+  if (TG >= 4 && ntg > 2)
+    contract_groups<DT, TG, U, VEC, EVEN_K, TWO>(w0, w1, xr, K, kg, acc0, acc1);
+  else if (TG >= 2 && ntg > 1)
+    contract_groups<DT, (TG >= 2 ? 2 : 1), U, VEC, EVEN_K, TWO>(w0, w1, xr, K, kg, acc0, acc1);
+  else
+    contract_groups<DT, 1, U, VEC, EVEN_K, TWO>(w0, w1, xr, K, kg, acc0, acc1);
 }
 
 // The expand of one projection, added into the base accumulators:
@@ -220,7 +254,9 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
     const int p = a.al.sorted_rows[blk * BM + tg * 16 + ri];
     ok[tg] = p < s.R;
     prow[tg] = p;
-    xr[tg] = static_cast<const DT *>(a.x) + (size_t)(ok[tg] ? p / s.k : 0) * H;
+    // padding rows read the block's first token (same lines as a real lane)
+    xr[tg] = static_cast<const DT *>(a.x) +
+             (size_t)(ok[tg] ? p / s.k : a.al.sorted_rows[blk * BM] / s.k) * H;
   }
   f32x4_t ag[TG], au[TG];
 #pragma unroll
@@ -228,7 +264,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
     ag[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     au[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, ok, active_groups<TG>(a, blk), H, kg, ag, au);
+  contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, active_groups<TG>(a, blk), H, kg, ag, au);
   if (MODE != 0)
     expand<DT, TG, VEC, true, MODE == 2>(a, blk, e, static_cast<const DT *>(a.B), (size_t)2 * I,
                                          nrow, (size_t)I, kg, ri, prow, ag, au);
@@ -296,12 +332,15 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   for (int tg = 0; tg < TG; ++tg) {
     prow[tg] = a.al.sorted_rows[blk * BM + tg * 16 + ri];
     ok[tg] = prow[tg] < s.R;  // padding rows contribute nothing
-    xr[tg] = static_cast<const DT *>(a.h) + ((size_t)blk * BM + tg * 16 + ri) * I;
+    // padding rows read the block's first row (always a routed row): the
+    // same lines as a real lane, so they coalesce instead of fetching
+    // unwritten rows of h
+    xr[tg] = static_cast<const DT *>(a.h) + ((size_t)blk * BM + (ok[tg] ? tg * 16 + ri : 0)) * I;
   }
   f32x4_t acc[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  contract<DT, TG, U, VEC, EVEN_K, false>(wd, wd, xr, ok, active_groups<TG>(a, blk), I, kg, acc, acc);
+  contract<DT, TG, U, VEC, EVEN_K, false>(wd, wd, xr, active_groups<TG>(a, blk), I, kg, acc, acc);
   if (MODE == 1)
     expand<DT, TG, VEC, false, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow, 0,
                                       kg, ri, prow, acc, acc);
@@ -499,11 +538,11 @@ __global__ __launch_bounds__(64) void k_combine_rows(Shape s, const int *__restr
 
 // ------------------------------------------------------------- dispatch
 
-// K-loop unroll (contraction steps in flight): 8 for 16-row blocks and for
-// the 32-row gate_up (two weight streams), else 4 (register pressure: the
-// 32-row down at 8 would drop to 3 waves per SIMD).
+// Contraction steps per register set of the double-buffered loop (two sets
+// in flight): 4 for 16- and 32-row blocks (6 for the 16-row down, which has
+// one weight stream), 2 for 64-row blocks.
 template <int TG, bool GATE_UP> constexpr int unroll_for() {
-  return TG == 1 || (TG == 2 && GATE_UP) ? 8 : 4;
+  return TG == 1 && !GATE_UP ? 6 : TG <= 2 ? 4 : 2;
 }
 
 template <typename DT, int TG, bool VEC, bool EK, int MODE>
