@@ -259,16 +259,39 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
   if (tid == 0) err_all = 0;
   __syncthreads();
 
+  // Each thread takes kHistBatch rows per pass with all their id loads in
+  // flight before the LDS atomics (a pass per row would pay the global load
+  // latency once per row).
+  constexpr int kHistBatch = 8;
   int err = 0;
-  for (int t = tid; t < T; t += kAlignThreads) atomicAdd(&tok_cnt[adapter_rank(aid, t, NA, err)], 1);
-  for (int p = tid; p < R; p += kAlignThreads) {
-    const int e = ids[p];
-    if (e < 0 || e >= E) {
-      err |= MOELORA_DEVERR_EXPERT_ID;
-      continue;
+  for (int t0 = tid; t0 < T; t0 += kHistBatch * kAlignThreads) {
+    int ar[kHistBatch];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      const int t = t0 + u * kAlignThreads;
+      ar[u] = t < T ? adapter_rank(aid, t, NA, err) : -1;
     }
-    int dummy = 0;
-    atomicAdd(&sm.hist[e * NR + adapter_rank(aid, p / k, NA, dummy)], 1);
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u)
+      if (ar[u] >= 0) atomicAdd(&tok_cnt[ar[u]], 1);
+  }
+  for (int p0 = tid; p0 < R; p0 += kHistBatch * kAlignThreads) {
+    int key[kHistBatch];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      const int p = p0 + u * kAlignThreads;
+      key[u] = -1;
+      if (p < R) {
+        const int e = ids[p];
+        int dummy = 0;
+        const int ar = adapter_rank(aid, p / k, NA, dummy);
+        if (e < 0 || e >= E) err |= MOELORA_DEVERR_EXPERT_ID;
+        else key[u] = e * NR + ar;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u)
+      if (key[u] >= 0) atomicAdd(&sm.hist[key[u]], 1);
   }
   if (err) atomicOr(&err_all, err);
   __syncthreads();
