@@ -31,6 +31,7 @@ struct moelora_plan_s {
   size_t ws_bytes;
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
   int raster_gb = 0;
+  int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
   int tiled_bk = 0;  // tiled GEMM: 0 = 8-wave kernel where K % 64 == 0; 32 / 64 = 4-wave slab width
   // stage timing
   bool timing = false;
@@ -76,15 +77,19 @@ int choose_tg(const moelora_desc &d, int T) {
   return kTgLarge;
 }
 
-// Waves (16 output columns each) per GEMM workgroup.  The decode weight
+// Waves per GEMM workgroup and weight rows per wave.  The decode weight
 // stream wants thousands of small workgroups: 64 weight rows per workgroup
-// (gate_up: 2 waves x (16 gate + 16 up) rows; down: 4 waves x 16 rows); the
-// same for 32-row blocks (measured best over 1, 2, 4 waves on both
-// medium-batch shapes within a few percent).
+// (gate_up: 2 waves x (16 gate + 16 up) rows; down: 4 waves x 16 rows).
+// 32-row blocks keep 64 rows per workgroup, but the down waves own two
+// 16-row tiles each (2 waves x 32 rows): two weight streams share each h
+// fragment, which measured 6-17 % faster there (and slower for 16-row
+// blocks).
 int choose_waves(int tg, bool gate_up) {
-  if (tg <= kTgMid) return gate_up ? 2 : 4;
+  if (tg == kTgSmall) return gate_up ? 2 : 4;
+  if (tg == kTgMid) return 2;
   return 4;
 }
+int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
 
 // Workgroups sharing one shrink tile's contraction: a decode step has only
 // tens of LoRA tiles, so each is split over several CUs.
@@ -248,6 +253,7 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   // tuning sweeps only: force the waves per GEMM workgroup (1..4)
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
+  if (const char *v = getenv("MOELORA_DOWN_ROWS")) p->down_rows = atoi(v) == 32 ? 32 : atoi(v) == 16 ? 16 : 0;
   if (const char *v = getenv("MOELORA_RASTER_GB")) p->raster_gb = std::max(0, atoi(v));
   if (const char *v = getenv("MOELORA_TILED_BK")) p->tiled_bk = atoi(v) == 64 ? 64 : atoi(v) == 32 ? 32 : 0;
   *plan = p;
@@ -295,12 +301,13 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   const GemmVariant vg = variant(d, tg, d.hidden, true), vd = variant(d, tg, d.inter, true);
   const int wgu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
   const int wd = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
+  const int down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
   snprintf(buf, buf_len,
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
-           "k_tail_d=%d waves_gu=%d waves_d=%d lora_mode=%s shrink_split=%d cap=%d "
+           "k_tail_d=%d waves_gu=%d waves_d=%d down_rows=%d lora_mode=%s shrink_split=%d cap=%d "
            "workspace=%zu",
            vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
-           k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd,
+           k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, tg == kTgTiled ? 0 : down_rows,
            d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile", L.split,
            L.s.cap, L.total);
   return MOELORA_OK;
@@ -399,6 +406,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   g.split = L.split;
   g.tiled_bk = plan->tiled_bk;
   g.raster_gb = plan->raster_gb;
+  g.down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
   g.zero_row = ws + L.off_zero;
   const bool t8 = tg == kTgTiled && plan->tiled_bk == 0;
   const int z2_gu = lora && t8 && fused_lora_ok(d, d.hidden);

@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
 // the down shrink of one routed row each, z_d[p] = h[pos_p] . A_d[a][e]^T,
 // alongside the base GEMM (both only need h); the expand then happens in
 // the combine.
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE>
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2>
 __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
@@ -321,10 +321,14 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   const int blk = gt.blk;
   const int e = a.al.block_expert[blk];
   const int I = s.I, H = s.H;
-  const int m0 = (gt.nt * a.waves + wave) * 16;
+  // R2: the wave owns two 16-row tiles (rows m0 .. m0+31), two weight
+  // streams against one set of h fragments
+  const int m0 = (gt.nt * a.waves + wave) * (R2 ? 32 : 16);
   if (e < 0 || m0 >= H) return;
   const int mrow = min(m0 + ri, H - 1);
+  const int mrow1 = R2 ? min(m0 + 16 + ri, H - 1) : mrow;
   const DT *wd = static_cast<const DT *>(a.W) + ((size_t)e * H + mrow) * I;
+  const DT *wd1 = static_cast<const DT *>(a.W) + ((size_t)e * H + mrow1) * I;
   const DT *xr[TG];
   bool ok[TG];
   int prow[TG];
@@ -337,24 +341,28 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
     // unwritten rows of h
     xr[tg] = static_cast<const DT *>(a.h) + ((size_t)blk * BM + (ok[tg] ? tg * 16 + ri : 0)) * I;
   }
-  f32x4_t acc[TG];
+  f32x4_t acc[TG], acc1[TG];
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg) acc[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  contract<DT, TG, U, VEC, EVEN_K, false>(wd, wd, xr, active_groups<TG>(a, blk), I, kg, acc, acc);
+  for (int tg = 0; tg < TG; ++tg) acc[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
   if (MODE == 1)
-    expand<DT, TG, VEC, false, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow, 0,
-                                      kg, ri, prow, acc, acc);
-  const int mb = m0 + kg * 4;
+    expand<DT, TG, VEC, R2, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow,
+                                   (size_t)(mrow1 - mrow), kg, ri, prow, acc, acc1);
 #pragma unroll
-  for (int tg = 0; tg < TG; ++tg) {
-    if (!ok[tg]) continue;
-    float *dst = a.y + (size_t)prow[tg] * H + mb;
-    if (VEC && mb + 3 < H) {
-      *reinterpret_cast<float4 *>(dst) = make_float4(acc[tg][0], acc[tg][1], acc[tg][2], acc[tg][3]);
-    } else {
+  for (int half = 0; half < (R2 ? 2 : 1); ++half) {
+    const int mb = m0 + 16 * half + kg * 4;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (mb + v < H) dst[v] = acc[tg][v];
+    for (int tg = 0; tg < TG; ++tg) {
+      if (!ok[tg]) continue;
+      const f32x4_t v4 = half ? acc1[tg] : acc[tg];
+      float *dst = a.y + (size_t)prow[tg] * H + mb;
+      if (VEC && mb + 3 < H) {
+        *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (mb + v < H) dst[v] = v4[v];
+      }
     }
   }
 }
@@ -555,11 +563,16 @@ hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_down(const GemmArgs &a, hipStream_t st) {
-  const int cols = 16 * a.waves;
+  const bool r2 = a.down_rows == 32;
+  const int cols = (r2 ? 32 : 16) * a.waves;
   const int ntn = (a.s.H + cols - 1) / cols;
   const int extra = MODE == 2 ? a.row_wgs : 0;
-  hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG, false>(), VEC, EK, MODE>),
-                     dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
+  if (r2)
+    hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE, true>),
+                       dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG, false>(), VEC, EK, MODE, false>),
+                       dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
   return hipGetLastError();
 }
 template <typename DT, int TG, bool VEC, bool EK, bool FROM_H>

@@ -54,6 +54,7 @@ SMALL = [
     (30, 128, 96, 8, 2, 3, 16, "bf16", "uniform_with_none"),    # 32-row blocks, row-wise LoRA
     (200, 128, 96, 64, 2, 3, 16, "bf16", "uniform_with_none"),  # 32-row blocks, tile-wise LoRA
     (60, 256, 128, 8, 2, 4, 16, "bf16", "uniform_with_none"),   # 64-row blocks, row-wise LoRA
+    (40, 136, 96, 8, 2, 3, 16, "bf16", "uniform_with_none"),    # 32-row blocks, H % 32 != 0 (down tiles clamped)
 ]
 
 
