@@ -80,13 +80,13 @@ int choose_tg(const moelora_desc &d, int T) {
 // Waves per GEMM workgroup and weight rows per wave.  The decode weight
 // stream wants thousands of small workgroups: 64 weight rows per workgroup
 // (gate_up: 2 waves x (16 gate + 16 up) rows; down: 4 waves x 16 rows).
-// 32-row blocks keep 64 rows per workgroup, but the down waves own two
-// 16-row tiles each (2 waves x 32 rows): two weight streams share each h
-// fragment, which measured 6-17 % faster there (and slower for 16-row
-// blocks).
+// 32-row blocks: gate_up workgroups of one wave (32 weight rows; measured
+// 1-2 % ahead of 2 and 4), and down waves that own two 16-row tiles each
+// (2 waves x 32 rows): two weight streams share each h fragment, which
+// measured 6-17 % faster there (and slower for 16-row blocks).
 int choose_waves(int tg, bool gate_up) {
   if (tg == kTgSmall) return gate_up ? 2 : 4;
-  if (tg == kTgMid) return 2;
+  if (tg == kTgMid) return gate_up ? 1 : 2;
   return 4;
 }
 int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
