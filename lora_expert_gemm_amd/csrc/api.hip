@@ -30,9 +30,7 @@ struct moelora_plan_s {
   moelora_desc d;
   size_t ws_bytes;
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
-  int raster_gb = 0;
   int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
-  int tiled_bk = 0;  // tiled GEMM: 0 = 8-wave kernel where K % 64 == 0; 32 / 64 = 4-wave slab width
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -254,8 +252,6 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_DOWN_ROWS")) p->down_rows = atoi(v) == 32 ? 32 : atoi(v) == 16 ? 16 : 0;
-  if (const char *v = getenv("MOELORA_RASTER_GB")) p->raster_gb = std::max(0, atoi(v));
-  if (const char *v = getenv("MOELORA_TILED_BK")) p->tiled_bk = atoi(v) == 64 ? 64 : atoi(v) == 32 ? 32 : 0;
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -404,11 +400,9 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   GemmArgs g{};
   g.s = s;
   g.split = L.split;
-  g.tiled_bk = plan->tiled_bk;
-  g.raster_gb = plan->raster_gb;
   g.down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
   g.zero_row = ws + L.off_zero;
-  const bool t8 = tg == kTgTiled && plan->tiled_bk == 0;
+  const bool t8 = tg == kTgTiled;
   const int z2_gu = lora && t8 && fused_lora_ok(d, d.hidden);
   const int z2_d = lora && t8 && fused_lora_ok(d, d.inter);
   g.topk_ids = ids;

@@ -64,8 +64,6 @@ struct GemmArgs {
   int row_wgs;             // row mode: leading workgroups that run rs
   int waves;               // waves per workgroup of the GEMM kernels (16 columns each)
   int down_rows;           // streaming down GEMM: weight rows per wave (16, or 32 = two tiles)
-  int raster_gb;           // 8-wave tiled GEMM: token blocks per workgroup raster group
-  int tiled_bk;            // tiled GEMM: 0 = 8-wave kernel where K % 64 == 0, else 4-wave slab (32 / 64)
   int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
                            // result (tiled shrink -> 8-wave GEMM); zero_row: 64 bf16 zeros
   void *zero_row;

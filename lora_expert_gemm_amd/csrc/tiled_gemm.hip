@@ -139,24 +139,6 @@ __device__ __forceinline__ void tile_finish(const GemmArgs &a, f32x16_t (&acc)[2
   }
 }
 
-// Workgroup id -> (token block, weight tile).  Ids run through groups of gb
-// consecutive token blocks; inside a group the blocks vary fastest, then the
-// weight tile.  The workgroups resident together on one XCD then share both
-// token blocks and weight tiles in that XCD's L2.  gb <= 0: blocks fastest
-// over the whole grid.
-__device__ __forceinline__ void tile_of(int id, int nblk, int ntn, int gb, int &blk, int &nt) {
-  if (gb <= 0 || gb >= nblk) {
-    blk = id % nblk;
-    nt = id / nblk;
-    return;
-  }
-  const int gsize = gb * ntn;
-  const int g = id / gsize, rem = id % gsize;
-  const int g0 = g * gb, gn = min(gb, nblk - g0);
-  blk = g0 + rem % gn;
-  nt = rem / gn;
-}
-
 template <int BK>
 struct Lds {
   static constexpr int kCpr = BK / 8;                // 16-byte chunks per row
@@ -331,8 +313,9 @@ __global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int li = lane & 31, lh = lane >> 5;
 
-  int blk, nt;
-  tile_of(xcd_remap(blockIdx.x, gridDim.x), s.nblk, gridDim.x / s.nblk, a.raster_gb, blk, nt);
+  const int Lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int blk = Lid % s.nblk, nt = Lid / s.nblk;  // blocks vary fastest: concurrent
+                                                     // workgroups share a weight tile
   const int e = a.al.block_expert[blk];
   if (e < 0) return;
   const int I = s.I, H = s.H;
@@ -645,14 +628,11 @@ hipError_t launch_tiled(const GemmArgs &a, bool gate_up, const GemmVariant &v, h
   if (a.s.nblk == 0) return hipSuccess;
   if (!v.bf16 || !v.vec || a.s.BM != kTM) return hipErrorInvalidValue;
   const int K = gate_up ? a.s.H : a.s.I;
-  if (a.tiled_bk == 0 && K % 64 == 0 && (!v.lora || a.z2))
+  if (K % 64 == 0 && (!v.lora || a.z2))
     return gate_up ? (v.lora ? go_tiled8<true, true>(a, st) : go_tiled8<true, false>(a, st))
                    : (v.lora ? go_tiled8<false, true>(a, st) : go_tiled8<false, false>(a, st));
-  const int bk = a.tiled_bk == 64 ? 64 : 32;
-  const bool even_k = K % bk == 0;
-  if (bk == 64)
-    return gate_up ? pick_tiled<true, 64>(a, even_k, v.lora, st) : pick_tiled<false, 64>(a, even_k, v.lora, st);
-  return gate_up ? pick_tiled<true, 32>(a, even_k, v.lora, st) : pick_tiled<false, 32>(a, even_k, v.lora, st);
+  return gate_up ? pick_tiled<true, 32>(a, K % 32 == 0, v.lora, st)
+                 : pick_tiled<false, 32>(a, K % 32 == 0, v.lora, st);
 }
 
 }  // namespace moelora
