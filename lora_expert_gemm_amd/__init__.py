@@ -23,6 +23,17 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build the HIP library first "
         "(python -m lora_expert_gemm_amd.build)")
 
+# One HIP runtime per process.  PyTorch for ROCm ships its own libamdhip64
+# (requested by the unversioned name libamdhip64.so); this library requests
+# libamdhip64.so.7.  Loaded after PyTorch, it binds to PyTorch's copy (same
+# soname); loaded first, it would pull in ROCm's copy and PyTorch would then
+# load a second runtime, and whichever initialises second finds no device.
+# So PyTorch, when installed, is imported before the library is loaded.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE = 0, -1, -2, -3, -4, -5

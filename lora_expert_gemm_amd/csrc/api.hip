@@ -208,6 +208,15 @@ int k_tail(const moelora_desc &d, int K) {
   return (ks - K % ks) % ks;
 }
 
+// A failed launch: MOELORA_ERR_HIP, and with MOELORA_VERBOSE set in the
+// environment a line on stderr naming the launch and the HIP error.
+moelora_status hip_failure(hipError_t err, const char *what, int line) {
+  if (getenv("MOELORA_VERBOSE"))
+    fprintf(stderr, "moelora_forward: %s (api.hip:%d) failed: %s (%d)\n", what, line,
+            hipGetErrorString(err), (int)err);
+  return MOELORA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,9 +381,10 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     *rec |= 1u << b;
     return hipEventRecord(ev[b], st);
   };
-#define MOELORA_TRY(expr)                    \
-  do {                                       \
-    if ((expr) != hipSuccess) return MOELORA_ERR_HIP; \
+#define MOELORA_TRY(expr)                                                            \
+  do {                                                                               \
+    const hipError_t moelora_err_ = (expr);                                          \
+    if (moelora_err_ != hipSuccess) return hip_failure(moelora_err_, #expr, __LINE__); \
   } while (0)
 
   const int waves_gu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
@@ -386,6 +396,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   float *z_d = reinterpret_cast<float *>(ws + L.off_zd);
   void *h = ws + L.off_h;
 
+  (void)hipGetLastError();  // an error left pending by an earlier call is not this call's
   MOELORA_TRY(mark());
   int *ids_ws = reinterpret_cast<int *>(ws + L.off_ids);
   float *w_ws = reinterpret_cast<float *>(ws + L.off_w);

@@ -155,3 +155,18 @@ def test_forward_rejects_small_workspace():
 def test_zero_tokens_is_a_noop():
     p = lib.Plan(**DECODE)
     _fwd(p, n_tokens=0)  # returns OK without any device work
+
+
+def test_binding_loads_torch_first():
+    """The package imports PyTorch (when installed) before loading the HIP
+    library, so both use one HIP runtime: loaded the other way round,
+    PyTorch brings a second runtime and one of them finds no device."""
+    import subprocess
+    import sys
+    code = ("import sys; import lora_expert_gemm_amd as L; "
+            "print(int('torch' in sys.modules))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
