@@ -184,6 +184,8 @@ def moelora_timing_end(plan):
 class Plan:
     """Owning wrapper of a plan handle."""
 
+    _destroy_fn = _lib.moelora_plan_destroy  # ctypes function object (holds the library)
+
     def __init__(self, max_tokens, hidden, inter, n_experts, top_k, n_adapters, rank,
                  dtype):
         self.handle, self.workspace_bytes = moelora_plan(
@@ -193,9 +195,11 @@ class Plan:
                          rank=rank, dtype=dtype)
 
     def __del__(self):
+        # the destroy function is held by the class: module globals may
+        # already be gone when a plan is collected at interpreter shutdown
         h = getattr(self, "handle", None)
         if h:
-            moelora_plan_destroy(h)
+            self._destroy_fn(h)
             self.handle = None
 
     def layout(self, n_tokens):

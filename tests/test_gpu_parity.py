@@ -55,6 +55,9 @@ SMALL = [
     (200, 128, 96, 64, 2, 3, 16, "bf16", "uniform_with_none"),  # 32-row blocks, tile-wise LoRA
     (60, 256, 128, 8, 2, 4, 16, "bf16", "uniform_with_none"),   # 64-row blocks, row-wise LoRA
     (40, 136, 96, 8, 2, 3, 16, "bf16", "uniform_with_none"),    # 32-row blocks, H % 32 != 0 (down tiles clamped)
+    (8, 64, 96, 1024, 32, 7, 256, "bf16", "uniform_with_none"), # maximum E, top-k and rank (row mode)
+    (64, 64, 64, 32, 2, 255, 8, "bf16", "uniform_with_none"),   # maximum adapters: 8192 alignment buckets
+    (300, 64, 64, 64, 2, 3, 256, "bf16", "uniform_with_none"),  # rank 256 in tile mode (split shrink)
 ]
 
 
