@@ -11,6 +11,7 @@ sample of the same workload.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -51,16 +52,25 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
-    """Hash of the device-kernel sources (everything in csrc but the host
-    ABI file), used to tell whether committed counters still apply."""
+def _code_only(text):
+    """Source text without comments and whitespace (kernel code is not
+    expected to hold "//" or "/*" inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
+def kernel_source_hash(csrc=None):
+    """Hash of the device-kernel code (everything in csrc but the host ABI
+    file, comments and whitespace ignored), used to tell whether committed
+    counters still apply."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "lora_expert_gemm_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "lora_expert_gemm_amd", "csrc")
     for n in sorted(os.listdir(csrc)):
         if n == "api.hip":
             continue
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(n.encode() + f.read())
+        with open(os.path.join(csrc, n)) as f:
+            h.update(n.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

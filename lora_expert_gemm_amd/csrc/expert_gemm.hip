@@ -19,12 +19,14 @@
 // register that feeds the MFMA.  The contraction index inside a chunk is
 // never interpreted: A and B chunks of a lane always cover the same indices.
 //
-// Work decomposition.  gate_up and down: one workgroup per (16 * waves
-// output columns, BM-row block); the expert's weight tile streams through
-// once per block, and blocks of the same expert sit on the same XCD so a
-// second block finds the tile in L2.  Small workgroups (one or two waves)
-// keep thousands of them in flight, which is what the weight stream of a
-// decode step needs.  Shrink: one workgroup per LoRA tile; its waves split
+// Work decomposition.  gate_up and down: one workgroup per (output columns
+// of its waves, BM-row block, BM = 16, 32 or 64); the expert's weight tile
+// streams through once per block, and blocks of the same expert sit on the
+// same XCD so a second block finds the tile in L2.  Small workgroups (one
+// to four waves) keep thousands of them in flight, which is what the weight
+// stream of a decode step needs.  A gate_up wave holds 16 gate and the 16
+// matching up rows; a down wave 16 rows, or two 16-row tiles that share
+// each h fragment (32-row blocks).  Shrink: one workgroup per LoRA tile; its waves split
 // the (16-row group of A, token group, contraction) work, and when the
 // contraction is split the partial sums meet in LDS and are added in a
 // fixed order, so results never depend on scheduling.
@@ -42,9 +44,6 @@ __device__ __forceinline__ u32x4_t ld(const DT *row, int k, int len) {
   return load_chunk_masked(row, k, len);
 }
 
-// acc[tg] += W_rows . X_rows^T over the contraction [0, K) for one or two
-// weight row pointers (TWO: gate and up), U steps of loads in flight.
-// Token rows with ok false contribute zeros.
 // acc[tg] += W_rows . X_rows^T over the whole contraction for NG token
 // groups.  Branch-free: every lane loads its operands unconditionally (a
 // padding row's x pointer aims at a valid row and its output column is never

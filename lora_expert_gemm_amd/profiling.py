@@ -132,8 +132,8 @@ def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
     lines = [f"# HBM traffic counters: {workload}", "",
              "Commands (run from /tmp with TMPDIR=/tmp; one counter per pass):", "", "```",
              command, "```", "",
-             f"Kernel sources: `{source_hash}` (sha256 prefix over the device-kernel sources, "
-             "as bench.py computes it).", "",
+             f"Kernel code: `{source_hash}` (sha256 prefix over the device-kernel sources with "
+             "comments and whitespace removed, as bench.py computes it).", "",
              f"Calibration: a plain {copy_mib} MiB device copy ({copy_kernel}) reports "
              f"FETCH_SIZE = {cf[copy_kernel]:.0f} KiB and WRITE_SIZE = {cw[copy_kernel]:.0f} KiB "
              f"per dispatch, so FETCH_SIZE is scaled by {fs:.4f} and WRITE_SIZE by {ws:.4f}.", "",
