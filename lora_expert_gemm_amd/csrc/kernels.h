@@ -97,9 +97,12 @@ struct GemmVariant {
                  // riding along and expand moved to the combine (down)
 };
 hipError_t launch_gate_up(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
-// LDS-tiled MFMA GEMM for 128-row blocks (bf16, 16-byte aligned rows).
+// LDS-tiled MFMA GEMM for 128-row blocks (bf16, 16-byte aligned rows): the
+// 8-wave kernel when the contraction is a multiple of 64 and the LoRA expand
+// (if any) reads z2 rows, else the 4-wave kernel.
 hipError_t launch_tiled(const GemmArgs &a, bool gate_up, const GemmVariant &v, hipStream_t st);
-// LDS-tiled LoRA shrink for 128-row blocks (bf16, r <= 64, r % 8 == 0, split 1).
+// LDS-tiled LoRA shrink for 128-row blocks (bf16, r <= 64, r % 8 == 0, split 1);
+// writes fp32 z, or z2 rows when a.z2.
 hipError_t launch_tiled_shrink(const GemmArgs &a, bool from_h, hipStream_t st);
 hipError_t launch_down(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
 // Shrink of every LoRA tile (partial sums of a.split contraction splits).

@@ -8,17 +8,23 @@
 // GEMM per expert), with the LoRA expand added into the base accumulators
 // (section "Kernel optimizations").
 //
-// Workgroup tile: 128 tokens (one alignment block) x 256 weight rows, 4
-// waves.  gate_up: rows 0..127 of the weight tile are gate rows n0..n0+127,
-// rows 128..255 the matching up rows, so wave w holds gate and up for
-// h-columns n0 + 32w .. +31 and forms SiLU(gate)*up in registers.  down:
-// wave w holds output rows m0 + 64w .. +63.  Each wave: 2 weight tiles x 4
-// token tiles of v_mfma_f32_32x32x16_bf16 (weights on the 32-row side).
+// Two kernels, both with v_mfma_f32_32x32x16_bf16 (weights on the 32-row
+// side, tokens on the 32-column side), SiLU(gate)*up formed in registers
+// (a wave holds the gate rows and the matching up rows of its h-columns):
 //
-// The contraction is staged through LDS in BK-wide slabs, double buffered:
-// the global loads of slab s+1 are issued (into registers) before the MFMAs
-// of slab s and written to the other LDS buffer after them; one barrier per
-// slab.  LDS rows are BK*2 bytes with XOR-swizzled 16-byte chunks.
+// k_tiled8 (contractions that are a multiple of 64): 128 tokens x 512
+// weight rows, 8 waves, one workgroup per CU; 64-wide slabs fetched with
+// global_load_lds_dwordx4 straight into two 80 KB LDS stages; the LoRA
+// expand runs as extra slabs of the same loop.
+//
+// k_tiled (the rest): 128 tokens x 256 weight rows, 4 waves, sized for two
+// workgroups per CU; 32-wide slabs staged through registers into double-buffered LDS
+// (the loads of slab s+1 are issued before the MFMAs of slab s and written
+// to the other buffer after them; one barrier per slab); the LoRA expand in
+// the epilogue.
+//
+// LDS rows hold one slab of one weight or token row with XOR-swizzled
+// 16-byte chunks.
 #include "common.h"
 #include "kernels.h"
 
