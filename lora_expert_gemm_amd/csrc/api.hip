@@ -31,6 +31,7 @@ struct moelora_plan_s {
   size_t ws_bytes;
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
   int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
+  int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -75,16 +76,18 @@ int choose_tg(const moelora_desc &d, int T) {
   return kTgLarge;
 }
 
-// Waves per GEMM workgroup and weight rows per wave.  The decode weight
-// stream wants thousands of small workgroups: 64 weight rows per workgroup
-// (gate_up: 2 waves x (16 gate + 16 up) rows; down: 4 waves x 16 rows).
-// 32-row blocks: gate_up workgroups of one wave (32 weight rows; measured
-// 1-2 % ahead of 2 and 4), and down waves that own two 16-row tiles each
-// (2 waves x 32 rows): two weight streams share each h fragment, which
-// measured 6-17 % faster there (and slower for 16-row blocks).
-int choose_waves(int tg, bool gate_up) {
-  if (tg == kTgSmall) return gate_up ? 2 : 4;
-  if (tg == kTgMid) return gate_up ? 1 : 2;
+// Waves per GEMM workgroup and weight rows per wave (measured with the
+// weight stream through the LDS ring).  16-row blocks: 4 waves for both
+// projections (gate_up: 4 x (16 gate + 16 up) rows, ~2.5 % ahead of 2 waves;
+// down: 4 x 16 rows).  32-row blocks: down waves that own two 16-row tiles
+// each (2 waves x 32 rows; two weight streams share each h fragment, 6-17 %
+// faster there and slower for 16-row blocks); gate_up workgroups of 4 waves
+// when the intermediate size is large (4 % ahead at 11008 columns) and of
+// one wave otherwise (8 % ahead at 768 columns, where a block has only 48
+// column tiles).
+int choose_waves(int tg, bool gate_up, int inter) {
+  if (tg == kTgSmall) return 4;
+  if (tg == kTgMid) return gate_up ? (inter >= 4096 ? 4 : 1) : 2;
   return 4;
 }
 int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
@@ -123,8 +126,8 @@ Layout make_layout(const moelora_desc &d, int T) {
   s.max_seg = (int)std::min<long long>(s.R, (long long)s.E * s.NA);
   s.max_tiles = s.nblk + s.max_seg;
   const int tg = s.BM / 16;
-  L.waves_gu = choose_waves(tg, true);
-  L.waves_d = choose_waves(tg, false);
+  L.waves_gu = choose_waves(tg, true, d.inter);
+  L.waves_d = choose_waves(tg, false, d.inter);
   L.split = choose_split(tg, s.R);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
   const size_t NB = (size_t)s.E * (s.NA + 1);
@@ -261,6 +264,7 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_DOWN_ROWS")) p->down_rows = atoi(v) == 32 ? 32 : atoi(v) == 16 ? 16 : 0;
+  if (const char *v = getenv("MOELORA_SLOTS")) p->slots = ring_slots_supported(atoi(v)) ? atoi(v) : 0;
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -412,6 +416,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   g.s = s;
   g.split = L.split;
   g.down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
+  g.slots = plan->slots;
   g.zero_row = ws + L.off_zero;
   const bool t8 = tg == kTgTiled;
   const int z2_gu = lora && t8 && fused_lora_ok(d, d.hidden);

@@ -133,6 +133,100 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
     contract_groups<DT, 1, U, VEC, EVEN_K, TWO>(w0, w1, xr, K, kg, acc0, acc1);
 }
 
+// Weight stream through LDS (bf16, contraction a multiple of 64).  A wave's
+// NW 16-row weight tiles are fetched in 64-wide slabs: slab j of tile t is
+// 16 rows x 128 bytes, brought by two global_load_lds_dwordx4 of 8 whole
+// rows each (lane l: row l / 8, one 16-byte chunk), so every load
+// instruction covers whole 128-byte lines -- the register path above has a
+// lane per (row, chunk of a 64-byte half line) and streams slower.  Slabs go
+// round a per-wave ring of S slots in LDS with S - 1 of them in flight; the
+// MFMA operand of lane l (row l % 16, chunk l / 16 of a 32-wide step) is then
+// one ds_read_b128.  Chunk c of tile row r sits at chunk c ^ (r % 8) of its
+// LDS row, so the 16 rows read at one chunk spread over distinct banks.
+// Tokens (L2-resident, shared by every workgroup of the block) are still
+// loaded straight into registers, one slab ahead.  Each slab issues the same
+// number of loads (past the end the last slab is fetched again into a free
+// slot), which makes a fixed vmcnt the wait for "slab j and its tokens".
+template <int NG, int NW, int S>
+__device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
+                                             const uint16_t *const *xr, int K, int kg, int ri,
+                                             unsigned char *ring, f32x4_t *acc0, f32x4_t *acc1) {
+  using M = Mma<uint16_t>;
+  constexpr int kSlot = NW * 2048;
+  constexpr int kYoung = 2 * NW + 2 * NG;  // loads issued after a slab's token loads
+  static_assert(kYoung < 16, "vmcnt immediate");
+  constexpr int kWait = 0x0f70 | kYoung;   // vmcnt(kYoung), expcnt / lgkmcnt unconstrained
+  const int nsl = K / 64;
+  auto dma = [&](int j, int p) {
+    unsigned char *d = ring + p * kSlot;
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(dsrc[2 * t + i] + 64 * j,
+                                         (__attribute__((address_space(3))) void *)(d + t * 2048 + i * 1024),
+                                         16, 0, 0);
+  };
+  struct Tok {
+    u32x4_t b[2][NG];
+  };
+  auto tload = [&](Tok &tk, int j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) tk.b[h][g] = load_chunk(xr[g], 64 * j + 32 * h + 8 * kg);
+  };
+  auto compute = [&](int p, const Tok &tk) {
+    const unsigned char *d = ring + p * kSlot + ri * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = ((4 * h + kg) ^ (ri & 7)) << 4;
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(d + c);
+      const u32x4_t a1 = NW == 2 ? *reinterpret_cast<const u32x4_t *>(d + 2048 + c) : a0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        M::step(acc0[g], a0, tk.b[h][g]);
+        if (NW == 2) M::step(acc1[g], a1, tk.b[h][g]);
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) dma(min(j, nsl - 1), j);
+  // one slab: fetch slab j + S - 1 and the tokens of slab j + 1, then the
+  // MFMAs of slab j once it and its tokens (tk) have arrived
+  auto step = [&](int j, const Tok &tk, Tok &tn) {
+    dma(min(j + S - 1, nsl - 1), (j + S - 1) % S);
+    tload(tn, min(j + 1, nsl - 1));
+    __builtin_amdgcn_s_waitcnt(kWait);
+    asm volatile("" ::: "memory");
+    compute(j % S, tk);
+  };
+  Tok ta, tb;
+  tload(ta, 0);
+  int j = 0;
+  for (; j + 2 <= nsl; j += 2) {
+    step(j, ta, tb);
+    step(j + 1, tb, ta);
+  }
+  if (j < nsl) step(j, ta, tb);
+  // vmcnt(0): no load of the ring may land after the wave leaves it
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
+// contract_dma over the block's ntg leading token groups.
+template <int TG, int NW, int S>
+__device__ __forceinline__ void contract_dma_groups(const uint16_t *const *dsrc,
+                                                    const uint16_t *const *xr, int ntg, int K, int kg,
+                                                    int ri, unsigned char *ring, f32x4_t *acc0,
+                                                    f32x4_t *acc1) {
+  if (TG >= 4 && ntg > 2)
+    contract_dma<TG, NW, S>(dsrc, xr, K, kg, ri, ring, acc0, acc1);
+  else if (TG >= 2 && ntg > 1)
+    contract_dma<(TG >= 2 ? 2 : 1), NW, S>(dsrc, xr, K, kg, ri, ring, acc0, acc1);
+  else
+    contract_dma<1, NW, S>(dsrc, xr, K, kg, ri, ring, acc0, acc1);
+}
+
 // The expand of one projection, added into the base accumulators:
 // acc[tg] += B_rows . z^T for the block's LoRA tiles.  z (float) feeds the
 // MFMA as a bf16 hi + lo pair (a split exact to about 2^-16) or as float.
@@ -229,8 +323,9 @@ __device__ __forceinline__ GemmTile gemm_tile(int nblk, int bid, int nb) {
 // (up), so SiLU * up is formed in registers.  h is written for the block's
 // real rows (padding rows are skipped by every reader).
 // MODE: 0 no LoRA, 1 tile-wise (z per sorted position, split partials),
-// 2 row-wise (z per routed row).
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE>
+// 2 row-wise (z per routed row).  S > 0: weights streamed through an S-slot
+// LDS ring per wave (contract_dma).
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, int S>
 __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
@@ -263,7 +358,23 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
     ag[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     au[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, active_groups<TG>(a, blk), H, kg, ag, au);
+  if constexpr (S > 0) {
+    // DMA rows: tile 0 = gate rows n0 .., tile 1 = the matching up rows
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint16_t *dsrc[4];  // [tile][instruction]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const uint16_t *g = static_cast<const uint16_t *>(a.W) +
+                          ((size_t)e * 2 * I + min(n0 + r, I - 1)) * H + 8 * ((lane & 7) ^ (r & 7));
+      dsrc[i] = g;
+      dsrc[2 + i] = g + (size_t)I * H;
+    }
+    contract_dma_groups<TG, 2, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
+                                  active_groups<TG>(a, blk), H, kg, ri, smem + wave * S * 4096, ag, au);
+  } else {
+    contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, active_groups<TG>(a, blk), H, kg, ag, au);
+  }
   if (MODE != 0)
     expand<DT, TG, VEC, true, MODE == 2>(a, blk, e, static_cast<const DT *>(a.B), (size_t)2 * I,
                                          nrow, (size_t)I, kg, ri, prow, ag, au);
@@ -295,7 +406,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
 // the down shrink of one routed row each, z_d[p] = h[pos_p] . A_d[a][e]^T,
 // alongside the base GEMM (both only need h); the expand then happens in
 // the combine.
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2>
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2, int S>
 __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
@@ -343,7 +454,24 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   f32x4_t acc[TG], acc1[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) acc[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
+  if constexpr (S > 0) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int NW = R2 ? 2 : 1;
+    const uint16_t *dsrc[2 * NW];  // [tile][instruction]
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 16 * t + 8 * i + (lane >> 3);
+        dsrc[2 * t + i] = static_cast<const uint16_t *>(a.W) + ((size_t)e * H + min(m0 + r, H - 1)) * I +
+                     8 * ((lane & 7) ^ (r & 7));
+      }
+    contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
+                                   active_groups<TG>(a, blk), I, kg, ri, smem + wave * S * NW * 2048,
+                                   acc, acc1);
+  } else {
+    contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
+  }
   if (MODE == 1)
     expand<DT, TG, VEC, R2, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow,
                                    (size_t)(mrow1 - mrow), kg, ri, prow, acc, acc1);
@@ -552,27 +680,60 @@ template <int TG, bool GATE_UP> constexpr int unroll_for() {
   return TG == 1 && !GATE_UP ? 6 : TG <= 2 ? 4 : 2;
 }
 
+template <typename DT, int TG, bool VEC, bool EK, int MODE, int S>
+hipError_t launch_gu(const GemmArgs &a, int ntn, hipStream_t st) {
+  auto kern = k_gate_up<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE, S>;
+  const int lds = S * 4096 * a.waves;  // two 16-row tiles (gate, up) per wave
+  if (S > 0) {
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3(ntn * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
+  return hipGetLastError();
+}
 template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
   const int cols = 16 * a.waves;
   const int ntn = (a.s.I + cols - 1) / cols;
-  hipLaunchKernelGGL((k_gate_up<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE>),
-                     dim3(ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
+  if constexpr (sizeof(DT) == 2 && VEC && EK) {
+    if (a.s.H % 64 == 0) {
+      if (a.slots == 3) return launch_gu<DT, TG, VEC, EK, MODE, 3>(a, ntn, st);
+      if (a.slots == 4) return launch_gu<DT, TG, VEC, EK, MODE, 4>(a, ntn, st);
+    }
+  }
+  return launch_gu<DT, TG, VEC, EK, MODE, 0>(a, ntn, st);
+}
+template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2, int S>
+hipError_t launch_d(const GemmArgs &a, int ntn, hipStream_t st) {
+  auto kern = k_down<DT, TG, unroll_for<TG, R2>(), VEC, EK, MODE, R2, S>;
+  const int extra = MODE == 2 ? a.row_wgs : 0;
+  const int lds = S * (R2 ? 4096 : 2048) * a.waves;
+  if (S > 0) {
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
   return hipGetLastError();
+}
+template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2>
+hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
+  if constexpr (sizeof(DT) == 2 && VEC && EK) {
+    if (a.s.I % 64 == 0) {
+      if (a.slots == 3) return launch_d<DT, TG, VEC, EK, MODE, R2, 3>(a, ntn, st);
+      if (a.slots == 4) return launch_d<DT, TG, VEC, EK, MODE, R2, 4>(a, ntn, st);
+    }
+  }
+  return launch_d<DT, TG, VEC, EK, MODE, R2, 0>(a, ntn, st);
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_down(const GemmArgs &a, hipStream_t st) {
   const bool r2 = a.down_rows == 32;
   const int cols = (r2 ? 32 : 16) * a.waves;
   const int ntn = (a.s.H + cols - 1) / cols;
-  const int extra = MODE == 2 ? a.row_wgs : 0;
-  if (r2)
-    hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE, true>),
-                       dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_down<DT, TG, unroll_for<TG, false>(), VEC, EK, MODE, false>),
-                       dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), 0, st, a);
-  return hipGetLastError();
+  return r2 ? go_down_r<DT, TG, VEC, EK, MODE, true>(a, ntn, st)
+            : go_down_r<DT, TG, VEC, EK, MODE, false>(a, ntn, st);
 }
 template <typename DT, int TG, bool VEC, bool EK, bool FROM_H>
 hipError_t go_shrink(const GemmArgs &a, hipStream_t st) {

@@ -64,6 +64,8 @@ struct GemmArgs {
   int row_wgs;             // row mode: leading workgroups that run rs
   int waves;               // waves per workgroup of the GEMM kernels (16 columns each)
   int down_rows;           // streaming down GEMM: weight rows per wave (16, or 32 = two tiles)
+  int slots;               // streaming GEMMs: LDS ring slots per wave for the weight stream
+                           // (bf16, contraction a multiple of 64); 0: loads into registers
   int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
                            // result (tiled shrink -> 8-wave GEMM); zero_row: 64 bf16 zeros
   void *zero_row;
@@ -71,6 +73,12 @@ struct GemmArgs {
   float *y;                // [R][H] down output per routed row
   AlignBufs al;
 };
+
+// LDS ring slots per wave of the streaming GEMMs' weight stream (bf16 with a
+// contraction that is a multiple of 64); the launchers hold instances for
+// the counts ring_slots_supported accepts, 0 meaning loads into registers.
+constexpr int kRingSlots = 3;
+inline bool ring_slots_supported(int s) { return s == 0 || s == 3 || s == 4; }
 
 // Shrink kernels: one workgroup of kShrinkWaves waves per LoRA tile.
 constexpr int kShrinkWaves = 16;

@@ -158,6 +158,38 @@ def test_stage_timing_hook():
     assert n == 3 and all(m >= 0 for m in ms) and ms[2] > 0 and ms[4] > 0
 
 
+# Streaming-block shapes whose contractions are multiples of 64, so the weight
+# stream can run through the LDS ring: 16-row blocks (row-wise LoRA), 32-row
+# blocks (row-wise, and tile-wise with two-tile down waves) and 64-row blocks.
+RING = [
+    (8, 256, 192, 8, 2, 3, 16),    # 16-row blocks
+    (30, 128, 128, 8, 2, 3, 32),   # 32-row blocks, row-wise LoRA
+    (200, 128, 192, 64, 2, 3, 16), # 32-row blocks, tile-wise LoRA
+    (100, 192, 128, 4, 2, 2, 16),  # 64-row blocks
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r", RING)
+def test_weight_stream_paths_agree(T, H, I, E, k, NA, r, monkeypatch):
+    """The LDS-ring weight stream (3 or 4 slots) and the register path feed
+    the MFMAs the same contraction indices in the same order, so the three
+    outputs are bitwise identical; each is also checked against the oracle."""
+    w = synth.Workload("ring", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
+                       adapters="uniform_with_none", seed=T * 11 + I)
+    d = synth.make_inputs(w)
+    rid, rw = oracle.ref_route(d["logits"], k)
+    ref = oracle_out(w, d, rid, rw)
+    outs = {}
+    for slots in ("0", "3", "4"):
+        monkeypatch.setenv("MOELORA_SLOTS", slots)
+        run = Run(w, d).forward()
+        say(f"[parity] ring slots={slots} {w}: plan {run.plan.info(T)}")
+        outs[slots] = run.out.cpu().numpy().copy()
+        check_close(run.out_f32(), ref, "bf16", f"slots {slots}")
+    assert np.array_equal(outs["0"], outs["3"])
+    assert np.array_equal(outs["0"], outs["4"])
+
+
 SAMPLES = {"tiny_fp32": 8, "decode_bf16": 16, "illustrative_bf16": 12,
            "prefill_bf16": 20, "many_expert_bf16": 48}
 
