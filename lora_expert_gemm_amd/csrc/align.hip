@@ -56,6 +56,36 @@ __device__ int block_excl_scan(int v, int *tmp, int *total) {
   return off + x - v;
 }
 
+// block_excl_scan of two values at once (same two barriers).
+__device__ int2 block_excl_scan2(int v0, int v1, int2 *tmp, int2 *total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int x0 = v0, x1 = v1;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y0 = __shfl_up(x0, d), y1 = __shfl_up(x1, d);
+    if (lane >= d) {
+      x0 += y0;
+      x1 += y1;
+    }
+  }
+  if (lane == kWave - 1) tmp[w] = make_int2(x0, x1);
+  __syncthreads();
+  int2 off = make_int2(0, 0), tot = make_int2(0, 0);
+#pragma unroll
+  for (int i = 0; i < kAlignWaves; ++i) {
+    const int2 u = tmp[i];
+    if (i < w) {
+      off.x += u.x;
+      off.y += u.y;
+    }
+    tot.x += u.x;
+    tot.y += u.y;
+  }
+  __syncthreads();
+  *total = tot;
+  return make_int2(off.x + x0 - v0, off.y + x1 - v1);
+}
+
 // Router for one token, computed by one wave: the k largest logits (ties to
 // the lower expert index, largest first) and their softmax over the kept
 // logits.  Lane l holds experts l, l + 64, ...; each of the k rounds takes
@@ -201,17 +231,24 @@ __device__ __forceinline__ int adapter_rank(const int *aid, int t, int NA, int &
   return (a >= 0 && a < NA) ? a : NA;
 }
 
+constexpr int kMaxExperts = 1024;
+
 struct AlignSmem {
   int hist[kMaxBuckets];  // rows per (expert, adapter rank) bucket
+  int seg0[kMaxExperts + 1];  // expert segment starts (align_plan on)
+  int rows[kMaxExperts];      // routed rows per expert
   int scan_tmp[kAlignWaves];
+  int2 scan_tmp2[kAlignWaves];
 };
 
 // Everything that follows from the bucket histogram (in LDS): padded expert
 // segments, bucket start positions, padding sentinels, block experts, LoRA
 // segments and their block tiles, the first tile of every block, and the
-// counts.  Thread e owns expert e from start to end, so nothing written to
-// global memory is read back, and two block scans place each expert's
-// segments and tiles.
+// counts.  Thread e owns expert e for the scans and the ordered LoRA segment
+// and tile lists, so nothing written to global memory is read back; the
+// bucket tables and the padding sentinels, which every thread can derive
+// from LDS, are written by the whole workgroup with neighbouring lanes on
+// neighbouring words.
 //
 // Two phases, because a workgroup barrier waits for every global store the
 // workgroup has in flight: align_plan runs the scans (barriers, LDS only)
@@ -232,6 +269,7 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
   int nseg_e = 0, ntile_e = 0;
   if (owner) {
     int run = 0;
+#pragma unroll 8
     for (int a = 0; a < NR; ++a) {
       const int c = hist[tid * NR + a];
       if (a < NA && c > 0) ++nseg_e;
@@ -242,7 +280,11 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
   }
   P.seg0 = block_excl_scan(P.padded, sm.scan_tmp, &P.num_padded);
   if (owner) {  // tiles depend on the absolute start of each bucket
+    sm.seg0[tid] = P.seg0;
+    sm.rows[tid] = P.rows;
+    if (tid == E - 1) sm.seg0[E] = P.num_padded;
     int run = P.seg0;
+#pragma unroll 8
     for (int a = 0; a < NR; ++a) {
       const int c = hist[tid * NR + a];
       if (a < NA && c > 0) ntile_e += (run + c - 1) / BM - run / BM + 1;
@@ -250,8 +292,12 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
       run += c;
     }
   }
-  P.seg_off = block_excl_scan(nseg_e, sm.scan_tmp, &P.n_seg);
-  P.tile_off = block_excl_scan(ntile_e, sm.scan_tmp, &P.n_tiles);  // ends with a barrier
+  int2 tot;
+  const int2 off = block_excl_scan2(nseg_e, ntile_e, sm.scan_tmp2, &tot);  // ends with a barrier
+  P.seg_off = off.x;
+  P.tile_off = off.y;
+  P.n_seg = tot.x;
+  P.n_tiles = tot.y;
   return P;
 }
 
@@ -261,16 +307,14 @@ __device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan
   const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, R = s.R;
   const int *start = sm.hist;
   if (tid < E) {
-    const int e = tid, seg0 = P.seg0, seg1 = P.seg0 + P.padded, end = P.seg0 + P.rows;
+    const int e = tid, seg0 = P.seg0, seg1 = P.seg0 + P.padded;
     al.seg_start[e] = seg0;
     int si = P.seg_off, ti = P.tile_off;
     int b_next = seg0 / BM;  // first block of e whose first tile is not yet written
-    for (int a = 0; a < NR; ++a) {
+    for (int a = 0; a < NA; ++a) {
       const int b = e * NR + a, st = start[b];
-      const int c = (a < NA ? start[b + 1] : end) - st;
-      al.bucket_base[b] = st;
-      al.bucket_cnt[b] = c;
-      if (a < NA && c > 0) {
+      const int c = start[b + 1] - st;
+      if (c > 0) {
         reinterpret_cast<int4 *>(al.lora_seg)[si++] = make_int4(e, a, st, c);
         for (int blk = st / BM; blk <= (st + c - 1) / BM; ++blk) {
           for (; b_next <= blk; ++b_next) al.block_tile_start[b_next] = ti;
@@ -280,10 +324,22 @@ __device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan
       }
     }
     for (; b_next < seg1 / BM; ++b_next) al.block_tile_start[b_next] = ti;
-    for (int i = end; i < seg1; ++i) al.sorted_rows[i] = R;
     for (int b = seg0 / BM; b < seg1 / BM; ++b) al.block_expert[b] = e;
   }
-  const int np = P.num_padded;
+  const int NB = E * NR, np = P.num_padded;
+  // bucket tables: start and row count of every (expert, adapter rank) bucket
+  for (int b = tid; b < NB; b += kAlignThreads) {
+    const int e = b / NR, a = b - e * NR, st = start[b];
+    const int end = a + 1 < NR ? start[b + 1] : sm.seg0[e] + sm.rows[e];
+    al.bucket_base[b] = st;
+    al.bucket_cnt[b] = end - st;
+  }
+  // padding sentinels: slot j < BM - 1 past the end of each expert's rows
+  for (int i = tid; i < E * (BM - 1); i += kAlignThreads) {
+    const int e = i / (BM - 1), j = i - e * (BM - 1);
+    const int pos = sm.seg0[e] + sm.rows[e] + j;
+    if (pos < sm.seg0[e + 1]) al.sorted_rows[pos] = R;
+  }
   if (tid == 0) {
     al.seg_start[E] = np;
     al.counts[0] = np;
