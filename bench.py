@@ -156,6 +156,33 @@ def cpu_baseline(w, d, target_s):
             "sample": f"oracle (C, float64, 1 thread) on {what} of {w.name}; {el:.1f} s"}
 
 
+def graph_replay(torch, step, stream, steps):
+    """The same layer call captured once in a HIP graph (no per-kernel launch
+    cost on replay) and replayed `steps` times; ms per replay, or the error."""
+    try:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()  # default priority
+        cap.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap):
+            step(cap)
+        stream.wait_stream(cap)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        log(f"[bench] hipGraph replay: {ms:.4f} ms/step")
+        return {"ms_per_step": ms}
+    except Exception as ex:  # reported, not fatal: the eager timing is the result
+        log(f"[bench] hipGraph capture failed: {ex}")
+        return {"ms_per_step": None, "error": str(ex)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -189,10 +216,10 @@ def main():
 
     lora = [None] * 4 if args.no_lora else [t["A_gu"], t["B_gu"], t["A_d"], t["B_d"]]
 
-    def step():
+    def step(st=None):
         L.moelora_forward(plan.handle, w.T, t["x"], t["logits"], None, None, t["adapter_ids"],
                           t["W_gu"], t["W_d"], *lora, out, ws, plan.workspace_bytes,
-                          stream.cuda_stream)
+                          (st or stream).cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -216,6 +243,8 @@ def main():
     st_ms, n_calls = L.moelora_timing_end(plan.handle)
     stage = {n: v / n_calls for n, v in zip(STAGES, st_ms)}
     log("[bench] stages (ms/call): " + ", ".join(f"{n}={v:.4f}" for n, v in stage.items()))
+
+    graph = graph_replay(torch, step, stream, args.steps)
 
     lay = plan.layout(w.T)
     torch.cuda.synchronize()
@@ -262,6 +291,7 @@ def main():
                   "TFLOP/s": alg["layer_flop"] / layer_s / 1e12,
                   "hbm_frac": alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS},
         "stages_ms": stage,
+        "graph": graph,
         "plan": plan.info(w.T),
         "kernel_source": kernel_source_hash(),
     }
