@@ -156,6 +156,44 @@ def cpu_baseline(w, d, target_s):
             "sample": f"oracle (C, float64, 1 thread) on {what} of {w.name}; {el:.1f} s"}
 
 
+def ceilings(torch, stream):
+    """What the same device reaches on plain work, timed here for context:
+    a 1 GiB device copy (bytes read + written per second) and a bf16
+    8192^3 torch.matmul (the vendor GEMM library)."""
+    res = {}
+    try:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["copy_GB/s"] = 2 * a.numel() * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        del a, b
+        n = 8192
+        x = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        y = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(x, y)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            torch.matmul(x, y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["gemm_bf16_TFLOP/s"] = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
+        del x, y
+    except Exception as ex:  # context only
+        res["error"] = str(ex)
+    log(f"[bench] ceilings: {res}")
+    return res
+
+
 def graph_replay(torch, step, stream, steps):
     """The same layer call captured once in a HIP graph (no per-kernel launch
     cost on replay) and replayed `steps` times; ms per replay, or the error."""
@@ -245,6 +283,7 @@ def main():
     log("[bench] stages (ms/call): " + ", ".join(f"{n}={v:.4f}" for n, v in stage.items()))
 
     graph = graph_replay(torch, step, stream, args.steps)
+    ceil = ceilings(torch, stream)
 
     lay = plan.layout(w.T)
     torch.cuda.synchronize()
@@ -263,6 +302,8 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": alg[f"{dom}_flop"] / dom_s / 1e12,
                 "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    ref = ceil.get("copy_GB/s" if decode else "gemm_bf16_TFLOP/s")
+    roof["frac_of_measured_ceiling"] = roof["achieved"] / ref if ref else None
     roof["traffic"] = None if args.no_lora else measured_traffic(w.name, dom)
     roof["launch_ms"] = stage[dom]
     roof["units_per_launch"] = {"experts": alg["n_exp"], "adapter_expert_pairs": alg["n_pair"],
@@ -292,6 +333,7 @@ def main():
                   "hbm_frac": alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS},
         "stages_ms": stage,
         "graph": graph,
+        "ceilings": ceil,
         "plan": plan.info(w.T),
         "kernel_source": kernel_source_hash(),
     }
