@@ -633,8 +633,11 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, const int *__restrict_
 // Row-wise LoRA variant: one thread per output column m, and each routed
 // row first gets its down expand, y[p][m] += sum_c z_d[p][c] B_d[a][e][m][c]
 // (linear, so it may follow the base GEMM in a later kernel).  A wave's 64
-// threads read 64 consecutive rows of B_d, i.e. one contiguous run.
-template <typename DT, bool VEC>
+// threads read 64 consecutive rows of B_d, i.e. one contiguous run.  The
+// loads of KB routed rows (KB = top-k up to 4) are issued together
+// (branch-free: a dropped row reads a valid address and is masked in the
+// sum), then the rows are added in ascending j.
+template <typename DT, bool VEC, int KB>
 __global__ __launch_bounds__(64) void k_combine_rows(Shape s, const int *__restrict__ ids,
                                                      const float *__restrict__ w,
                                                      const float *__restrict__ y, DT *out,
@@ -647,26 +650,44 @@ __global__ __launch_bounds__(64) void k_combine_rows(Shape s, const int *__restr
   const int H = s.H, r = s.r;
   if (m >= H) return;
   int ad = aid[t];
-  if (ad < 0 || ad >= s.NA) ad = -1;
+  const bool lora = ad >= 0 && ad < s.NA;
+  if (!lora) ad = 0;
   float acc = 0.f;
-  for (int j = 0; j < s.k; ++j) {
-    const int p = t * s.k + j;
-    const int e = ids[p];
-    if (e < 0 || e >= s.E) continue;
-    float v = y[(size_t)p * H + m];
-    if (ad >= 0) {
-      const float *zp = z_d + (size_t)p * r;
-      const DT *b = B_d + (((size_t)ad * s.E + e) * H + m) * r;
-      float sum = 0.f;
-      for (int c = 0; c < r; c += EPC) {
-        const Chunk<DT> bc = chunk_elems<DT>(load_chunk_any<DT, VEC>(b, c, r));
+  for (int j0 = 0; j0 < s.k; j0 += KB) {
+    float v[KB], wt[KB];
+    bool ok[KB];
+    const DT *b[KB];
+    const float *zp[KB];
 #pragma unroll
-        for (int u = 0; u < EPC; ++u)
-          if (VEC || c + u < r) sum = __builtin_fmaf(zp[c + u], Elem<DT>::to_f32(bc.v[u]), sum);
-      }
-      v += sum;
+    for (int u = 0; u < KB; ++u) {
+      const int j = min(j0 + u, s.k - 1), p = t * s.k + j;
+      const int e = ids[p];
+      ok[u] = j0 + u < s.k && e >= 0 && e < s.E;
+      const int ee = ok[u] ? e : 0, pp = ok[u] ? p : t * s.k;
+      v[u] = y[(size_t)pp * H + m];
+      wt[u] = w[pp];
+      b[u] = B_d + (((size_t)ad * s.E + ee) * H + m) * r;
+      zp[u] = z_d + (size_t)pp * r;
     }
-    acc += w[p] * v;
+    if (lora) {
+      float sum[KB] = {};
+      for (int c = 0; c < r; c += EPC) {
+        Chunk<DT> bc[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) bc[u] = chunk_elems<DT>(load_chunk_any<DT, VEC>(b[u], c, r));
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+#pragma unroll
+          for (int q = 0; q < EPC; ++q)
+            if (VEC || c + q < r)
+              sum[u] = __builtin_fmaf(zp[u][c + q], Elem<DT>::to_f32(bc[u].v[q]), sum[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) v[u] += sum[u];
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      if (ok[u]) acc += wt[u] * v[u];
   }
   out[(size_t)t * H + m] = Elem<DT>::from_f32(acc);
 }
@@ -805,14 +826,21 @@ hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const 
   if (s.T == 0) return hipSuccess;
   if (z_d) {
     const dim3 grid(s.T, (s.H + 63) / 64);
-#define MOELORA_COMB(DT, V)                                                                    \
-  hipLaunchKernelGGL((k_combine_rows<DT, V>), grid, dim3(64), 0, st, s, ids, w, y,             \
+#define MOELORA_COMB(DT, V, KB)                                                                \
+  hipLaunchKernelGGL((k_combine_rows<DT, V, KB>), grid, dim3(64), 0, st, s, ids, w, y,         \
                      static_cast<DT *>(out), z_d, static_cast<const DT *>(B_d), adapter_ids)
+#define MOELORA_COMB_K(DT, V)                                                                  \
+  do {                                                                                         \
+    if (s.k == 1) MOELORA_COMB(DT, V, 1);                                                      \
+    else if (s.k == 2) MOELORA_COMB(DT, V, 2);                                                 \
+    else MOELORA_COMB(DT, V, 4);                                                               \
+  } while (0)
     if (bf16) {
-      if (vec) MOELORA_COMB(uint16_t, true); else MOELORA_COMB(uint16_t, false);
+      if (vec) MOELORA_COMB_K(uint16_t, true); else MOELORA_COMB_K(uint16_t, false);
     } else {
-      if (vec) MOELORA_COMB(float, true); else MOELORA_COMB(float, false);
+      if (vec) MOELORA_COMB_K(float, true); else MOELORA_COMB_K(float, false);
     }
+#undef MOELORA_COMB_K
 #undef MOELORA_COMB
     return hipGetLastError();
   }
