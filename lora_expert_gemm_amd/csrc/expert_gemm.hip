@@ -15,9 +15,13 @@
 // the block's tokens on the 16-column side, so a decode block with one or
 // two tokens still fills the matrix core's rows with weights (the operand
 // swap of the aib.vote news item on SageMaker MoE kernel optimizations,
-// first item), and each weight element is loaded once, straight into the
-// register that feeds the MFMA.  The contraction index inside a chunk is
-// never interpreted: A and B chunks of a lane always cover the same indices.
+// first item), and each weight element is loaded once: in bf16 with a
+// contraction that is a multiple of 64 through a small per-wave LDS ring
+// filled with whole-line loads (contract_dma), otherwise straight into the
+// register that feeds the MFMA (contract_groups).  The contraction index
+// inside a chunk is never interpreted: A and B chunks of a lane always cover
+// the same indices, and both paths feed the MFMAs the same indices in the
+// same order.
 //
 // Work decomposition.  gate_up and down: one workgroup per (output columns
 // of its waves, BM-row block, BM = 16, 32 or 64); the expert's weight tile
