@@ -245,6 +245,65 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, const 
   const Shape &s = a.s;
   const int r = s.r;
   const int t0 = a.al.block_tile_start[blk], t1 = a.al.block_tile_start[blk + 1];
+  if constexpr (ROWZ && VEC) {
+    if (r <= KS) {
+      // One contraction step per tile (r <= 32): the B chunks and z values of
+      // four tiles are loaded together, then their MFMAs run in tile order.
+      // Loads are unconditional (a lane past the rank or a token outside the
+      // tile reads a valid address and its value is zeroed).
+      constexpr int TB = 4;
+      const int kk = kg * EPC, kc = kk < r ? kk : 0;
+      const bool kin = kk < r;
+      for (int tb = t0; tb < t1; tb += TB) {
+        int4 tl[TB];
+        u32x4_t c0[TB], c1[TB];
+        float zv[TB][TG][EPC];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          tl[u] = reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + u, t1 - 1)];
+          const DT *b0 = Bbase + (((size_t)tl[u].y * s.E + e) * b_rows + row) * r;
+          c0[u] = load_chunk(b0, kc);
+          c1[u] = TWO ? load_chunk(b0 + row_off1 * r, kc) : c0[u];
+#pragma unroll
+          for (int tg = 0; tg < TG; ++tg) {
+            const float *zp = a.z + (size_t)(prow[tg] < s.R ? prow[tg] : 0) * r + kc;
+#pragma unroll
+            for (int q = 0; q < EPC; q += 4) {
+              const float4 v4 = *reinterpret_cast<const float4 *>(zp + q);
+              zv[u][tg][q] = v4.x;
+              zv[u][tg][q + 1] = v4.y;
+              zv[u][tg][q + 2] = v4.z;
+              zv[u][tg][q + 3] = v4.w;
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          if (tb + u >= t1) break;
+          const int lo = tl[u].z, n = tl[u].w;
+          const u32x4_t a0 = kin ? c0[u] : u32x4_t{0, 0, 0, 0};
+          const u32x4_t a1 = kin ? c1[u] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int tg = 0; tg < TG; ++tg) {
+            const int local = tg * 16 + ri;
+            const bool in = kin && local >= lo && local < lo + n;
+            float z[EPC];
+#pragma unroll
+            for (int q = 0; q < EPC; ++q) z[q] = in ? zv[u][tg][q] : 0.f;
+            u32x4_t zh, zl;
+            SplitF32<DT>::run(z, zh, zl);
+            M::step(acc0[tg], a0, zh);
+            if (TWO) M::step(acc1[tg], a1, zh);
+            if constexpr (sizeof(DT) == 2) {
+              M::step(acc0[tg], a0, zl);
+              if (TWO) M::step(acc1[tg], a1, zl);
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
   for (int ti = t0; ti < t1; ++ti) {
     const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[ti];
     const int ad = tl.y, lo = tl.z, n = tl.w;
