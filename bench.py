@@ -90,10 +90,14 @@ def measured_traffic(workload, stage):
     return v["bytes"] if v else None
 
 
-def algorithmic(w, ids, aid):
+def algorithmic(w, ids, aid, row_mode=False):
     """Bytes and FLOPs the method must move / compute for one call: weights of
     the experts and (adapter, expert) pairs routed to, x read, out written;
-    FLOPs of the routed rows (padding and elementwise work excluded)."""
+    FLOPs of the routed rows (padding and elementwise work excluded).  Per
+    kernel: gate_up holds the base GEMM and the expand (its shrink runs
+    before it); the down launch holds the base GEMM and the expand, or, with
+    row-wise LoRA, the base GEMM and the down shrink (the expand then runs in
+    the combine)."""
     s = 2 if w.dtype == "bf16" else 4
     T, H, I, k, r = w.T, w.H, w.I, w.k, w.r
     valid = (ids >= 0) & (ids < w.E)
@@ -110,8 +114,12 @@ def algorithmic(w, ids, aid):
     # y out)
     gu_bytes = s * (n_exp * 2 * I * H + n_pair * 2 * I * r + T * H + R * I) + 4 * R_lora * r
     gu_flop = R * 4 * H * I + R_lora * 4 * I * r
-    dn_bytes = s * (n_exp * H * I + n_pair * H * r + R * I) + 4 * R * H + 4 * R_lora * r
-    dn_flop = R * 2 * H * I + R_lora * 2 * H * r
+    if row_mode:  # A_d read, z_d written by the shrinks riding along
+        dn_bytes = s * (n_exp * H * I + n_pair * I * r + R * I) + 4 * R * H + 4 * R_lora * r
+        dn_flop = R * 2 * H * I + R_lora * 2 * I * r
+    else:         # B_d read, z_d read by the expand
+        dn_bytes = s * (n_exp * H * I + n_pair * H * r + R * I) + 4 * R * H + 4 * R_lora * r
+        dn_flop = R * 2 * H * I + R_lora * 2 * H * r
     return dict(n_exp=n_exp, n_pair=n_pair, R=R, R_lora=R_lora, layer_bytes=layer_bytes,
                 layer_flop=layer_flop, gate_up_bytes=gu_bytes, gate_up_flop=gu_flop,
                 down_bytes=dn_bytes, down_flop=dn_flop)
@@ -290,7 +298,7 @@ def main():
     ids = ws[lay["off_topk_ids"]: lay["off_topk_ids"] + 4 * w.T * w.k].cpu().numpy() \
         .view(np.int32).reshape(w.T, w.k)
     alg = algorithmic(w, ids, d["adapter_ids"] if not args.no_lora
-                      else np.full(w.T, -1, np.int32))
+                      else np.full(w.T, -1, np.int32), "lora_mode=row" in plan.info(w.T))
 
     decode = w.T * w.k <= 24 * w.E
     dom = max(("gate_up", "down"), key=lambda n: stage[n])
