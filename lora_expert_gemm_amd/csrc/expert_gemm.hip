@@ -151,6 +151,7 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
 // loaded straight into registers, one slab ahead.  Each slab issues the same
 // number of loads (past the end the last slab is fetched again into a free
 // slot), which makes a fixed vmcnt the wait for "slab j and its tokens".
+// Weight loads are marked non-temporal: each line is read once.
 template <int NG, int NW, int S>
 __device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
                                              const uint16_t *const *xr, int K, int kg, int ri,
@@ -169,7 +170,7 @@ __device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
       for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_global_load_lds(dsrc[2 * t + i] + 64 * j,
                                          (__attribute__((address_space(3))) void *)(d + t * 2048 + i * 1024),
-                                         16, 0, 0);
+                                         16, 0, kCpolNonTemporal);
   };
   struct Tok {
     u32x4_t b[2][NG];
