@@ -232,51 +232,76 @@ __device__ __forceinline__ void contract_dma_groups(const uint16_t *const *dsrc,
     contract_dma<1, NW, S>(dsrc, xr, K, kg, ri, ring, acc0, acc1);
 }
 
+// z values of a lane's rows for the batched expand below: row mode, z of
+// routed row prow[tg]; tile mode (one contraction split), z of sorted
+// position blk * BM + tg * 16 + ri.  Neither depends on the LoRA tile, so
+// they are loaded once, before the base contraction, and their latency
+// hides under it.  A padding row reads row 0 / its own unused position; its
+// value is never selected.
+template <typename DT, int TG>
+struct ZRows {
+  float v[TG][Elem<DT>::kPerChunk];
+};
+
+template <typename DT, bool VEC, bool ROWZ>
+__device__ __forceinline__ bool expand_batched(const GemmArgs &a) {
+  return VEC && a.s.r <= Mma<DT>::kK && (ROWZ || a.split == 1);
+}
+
+template <typename DT, int TG, bool ROWZ>
+__device__ __forceinline__ void load_zrows(const GemmArgs &a, int blk, int kg, int ri,
+                                           const int *prow, ZRows<DT, TG> &z) {
+  constexpr int EPC = Elem<DT>::kPerChunk;
+  const int r = a.s.r, kk = kg * EPC, kc = kk < r ? kk : 0;
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    const size_t row = ROWZ ? (size_t)(prow[tg] < a.s.R ? prow[tg] : 0)
+                            : (size_t)blk * 16 * TG + tg * 16 + ri;
+    const float *zp = a.z + row * r + kc;
+#pragma unroll
+    for (int q = 0; q < EPC; q += 4) {
+      const float4 v4 = *reinterpret_cast<const float4 *>(zp + q);
+      z.v[tg][q] = v4.x;
+      z.v[tg][q + 1] = v4.y;
+      z.v[tg][q + 2] = v4.z;
+      z.v[tg][q + 3] = v4.w;
+    }
+  }
+}
+
 // The expand of one projection, added into the base accumulators:
-// acc[tg] += B_rows . z^T for the block's LoRA tiles.  z (float) feeds the
-// MFMA as a bf16 hi + lo pair (a split exact to about 2^-16) or as float.
+// acc[tg] += B_rows . z^T for the block's LoRA tiles t0 .. t1-1.  z (float)
+// feeds the MFMA as a bf16 hi + lo pair (a split exact to about 2^-16) or
+// as float.
 template <typename DT, int TG, bool VEC, bool TWO, bool ROWZ>
-__device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, const DT *Bbase,
-                                       size_t b_rows, int row, size_t row_off1, int kg, int ri,
-                                       const int *prow, f32x4_t *acc0, f32x4_t *acc1) {
+__device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0, int t1,
+                                       const ZRows<DT, TG> &zr, const DT *Bbase, size_t b_rows,
+                                       int row, size_t row_off1, int kg, int ri, const int *prow,
+                                       f32x4_t *acc0, f32x4_t *acc1) {
   using M = Mma<DT>;
   constexpr int EPC = Elem<DT>::kPerChunk;
   constexpr int KS = M::kK;
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
   const int r = s.r;
-  const int t0 = a.al.block_tile_start[blk], t1 = a.al.block_tile_start[blk + 1];
-  if constexpr (ROWZ && VEC) {
-    if (r <= KS) {
-      // One contraction step per tile (r <= 32): the B chunks and z values of
-      // four tiles are loaded together, then their MFMAs run in tile order.
-      // Loads are unconditional (a lane past the rank or a token outside the
-      // tile reads a valid address and its value is zeroed).
+  if constexpr (VEC) {
+    if (expand_batched<DT, VEC, ROWZ>(a)) {
+      // One contraction step per tile (r <= KS), z already in registers:
+      // the descriptors and B chunks of four tiles are loaded together,
+      // then their MFMAs run in tile order.  Loads are unconditional (a
+      // lane past the rank reads a valid address and its value is zeroed).
       constexpr int TB = 4;
       const int kk = kg * EPC, kc = kk < r ? kk : 0;
       const bool kin = kk < r;
       for (int tb = t0; tb < t1; tb += TB) {
         int4 tl[TB];
         u32x4_t c0[TB], c1[TB];
-        float zv[TB][TG][EPC];
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
           tl[u] = reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + u, t1 - 1)];
           const DT *b0 = Bbase + (((size_t)tl[u].y * s.E + e) * b_rows + row) * r;
           c0[u] = load_chunk(b0, kc);
           c1[u] = TWO ? load_chunk(b0 + row_off1 * r, kc) : c0[u];
-#pragma unroll
-          for (int tg = 0; tg < TG; ++tg) {
-            const float *zp = a.z + (size_t)(prow[tg] < s.R ? prow[tg] : 0) * r + kc;
-#pragma unroll
-            for (int q = 0; q < EPC; q += 4) {
-              const float4 v4 = *reinterpret_cast<const float4 *>(zp + q);
-              zv[u][tg][q] = v4.x;
-              zv[u][tg][q + 1] = v4.y;
-              zv[u][tg][q + 2] = v4.z;
-              zv[u][tg][q + 3] = v4.w;
-            }
-          }
         }
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
@@ -290,7 +315,7 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, const 
             const bool in = kin && local >= lo && local < lo + n;
             float z[EPC];
 #pragma unroll
-            for (int q = 0; q < EPC; ++q) z[q] = in ? zv[u][tg][q] : 0.f;
+            for (int q = 0; q < EPC; ++q) z[q] = in ? zr.v[tg][q] : 0.f;
             u32x4_t zh, zl;
             SplitF32<DT>::run(z, zh, zl);
             M::step(acc0[tg], a0, zh);
@@ -416,6 +441,15 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
     xr[tg] = static_cast<const DT *>(a.x) +
              (size_t)(ok[tg] ? p / s.k : a.al.sorted_rows[blk * BM] / s.k) * H;
   }
+  // LoRA tiles of the block and (batched expand) the lane's z values,
+  // fetched ahead of the contraction
+  int t0 = 0, t1 = 0;
+  ZRows<DT, TG> zr{};
+  if (MODE != 0) {
+    t0 = a.al.block_tile_start[blk];
+    t1 = a.al.block_tile_start[blk + 1];
+    if (expand_batched<DT, VEC, MODE == 2>(a)) load_zrows<DT, TG, MODE == 2>(a, blk, kg, ri, prow, zr);
+  }
   f32x4_t ag[TG], au[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
@@ -440,8 +474,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
     contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, active_groups<TG>(a, blk), H, kg, ag, au);
   }
   if (MODE != 0)
-    expand<DT, TG, VEC, true, MODE == 2>(a, blk, e, static_cast<const DT *>(a.B), (size_t)2 * I,
-                                         nrow, (size_t)I, kg, ri, prow, ag, au);
+    expand<DT, TG, VEC, true, MODE == 2>(a, blk, e, t0, t1, zr, static_cast<const DT *>(a.B),
+                                         (size_t)2 * I, nrow, (size_t)I, kg, ri, prow, ag, au);
   DT *hout = static_cast<DT *>(a.h);
   const int nb = n0 + kg * 4;
 #pragma unroll
@@ -515,6 +549,13 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
     // unwritten rows of h
     xr[tg] = static_cast<const DT *>(a.h) + ((size_t)blk * BM + (ok[tg] ? tg * 16 + ri : 0)) * I;
   }
+  int t0 = 0, t1 = 0;
+  ZRows<DT, TG> zr{};
+  if (MODE == 1) {
+    t0 = a.al.block_tile_start[blk];
+    t1 = a.al.block_tile_start[blk + 1];
+    if (expand_batched<DT, VEC, false>(a)) load_zrows<DT, TG, false>(a, blk, kg, ri, prow, zr);
+  }
   f32x4_t acc[TG], acc1[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) acc[tg] = acc1[tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -537,8 +578,8 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
     contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
   }
   if (MODE == 1)
-    expand<DT, TG, VEC, R2, false>(a, blk, e, static_cast<const DT *>(a.B), (size_t)H, mrow,
-                                   (size_t)(mrow1 - mrow), kg, ri, prow, acc, acc1);
+    expand<DT, TG, VEC, R2, false>(a, blk, e, t0, t1, zr, static_cast<const DT *>(a.B), (size_t)H,
+                                   mrow, (size_t)(mrow1 - mrow), kg, ri, prow, acc, acc1);
 #pragma unroll
   for (int half = 0; half < (R2 ? 2 : 1); ++half) {
     const int mb = m0 + 16 * half + kg * 4;
