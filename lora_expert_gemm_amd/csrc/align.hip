@@ -232,11 +232,15 @@ __device__ __forceinline__ int adapter_rank(const int *aid, int t, int NA, int &
 }
 
 constexpr int kMaxExperts = 1024;
+// buckets per thread in align_plan / align_store (consecutive buckets)
+constexpr int kBucketChunk = (kMaxBuckets + kAlignThreads - 1) / kAlignThreads;
 
 struct AlignSmem {
-  int hist[kMaxBuckets];  // rows per (expert, adapter rank) bucket
-  int seg0[kMaxExperts + 1];  // expert segment starts (align_plan on)
+  int hist[kMaxBuckets];      // rows per (expert, adapter rank) bucket; after align_plan its start
+  int seg0[kMaxExperts + 1];  // padded expert segment starts, seg0[E] = padded total
   int rows[kMaxExperts];      // routed rows per expert
+  int p0[kMaxExperts];        // rows of the experts before e (unpadded)
+  int tile0[kMaxExperts];     // index of expert e's first LoRA tile
   int scan_tmp[kAlignWaves];
   int2 scan_tmp2[kAlignWaves];
 };
@@ -244,60 +248,112 @@ struct AlignSmem {
 // Everything that follows from the bucket histogram (in LDS): padded expert
 // segments, bucket start positions, padding sentinels, block experts, LoRA
 // segments and their block tiles, the first tile of every block, and the
-// counts.  Thread e owns expert e for the scans and the ordered LoRA segment
-// and tile lists, so nothing written to global memory is read back; the
-// bucket tables and the padding sentinels, which every thread can derive
-// from LDS, are written by the whole workgroup with neighbouring lanes on
-// neighbouring words.
+// counts.  Thread i takes the consecutive buckets [b0, b0 + nb) (bucket
+// order is (expert, adapter rank)), so the LoRA segment and tile lists, which
+// follow bucket order, come out of three block-wide scans with no serial
+// loop over an expert's buckets; a block finds its expert by binary search
+// over the segment starts.
 //
 // Two phases, because a workgroup barrier waits for every global store the
 // workgroup has in flight: align_plan runs the scans (barriers, LDS only)
 // and turns sm.hist[b] into the start position of bucket b; align_store
 // then issues every global store with no barrier after it.
 struct AlignPlan {
-  int seg0, rows, padded;       // owner thread: its expert's segment
-  int seg_off, tile_off;        // owner thread: first LoRA segment / tile
+  int c[kBucketChunk];        // row counts of the thread's buckets
+  int b0, nb;                 // the thread's buckets
+  int seg_off, tile_off;      // first LoRA segment / tile of the thread's buckets
   int num_padded, n_seg, n_tiles;
 };
 
 __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
   const int tid = threadIdx.x;
-  const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM;
+  const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, NB = E * NR;
   int *hist = sm.hist;
-  const bool owner = tid < E;  // E <= 1024: one expert per thread
   AlignPlan P{};
-  int nseg_e = 0, ntile_e = 0;
-  if (owner) {
-    int run = 0;
-#pragma unroll 8
-    for (int a = 0; a < NR; ++a) {
-      const int c = hist[tid * NR + a];
-      if (a < NA && c > 0) ++nseg_e;
-      run += c;
-    }
-    P.rows = run;
-    P.padded = (run + BM - 1) / BM * BM;
+  const int per = (NB + kAlignThreads - 1) / kAlignThreads;
+  P.b0 = min(tid * per, NB);
+  P.nb = min(per, NB - P.b0);
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kBucketChunk; ++i) {
+    P.c[i] = i < P.nb ? hist[P.b0 + i] : 0;
+    sum += P.c[i];
   }
-  P.seg0 = block_excl_scan(P.padded, sm.scan_tmp, &P.num_padded);
-  if (owner) {  // tiles depend on the absolute start of each bucket
-    sm.seg0[tid] = P.seg0;
-    sm.rows[tid] = P.rows;
-    if (tid == E - 1) sm.seg0[E] = P.num_padded;
-    int run = P.seg0;
-#pragma unroll 8
-    for (int a = 0; a < NR; ++a) {
-      const int c = hist[tid * NR + a];
-      if (a < NA && c > 0) ntile_e += (run + c - 1) / BM - run / BM + 1;
-      hist[tid * NR + a] = run;  // bucket start from here on
-      run += c;
+  // unpadded start of every bucket (its counts are read: the scan's barriers
+  // order the overwrite after every thread's read)
+  int total;
+  int run = block_excl_scan(sum, sm.scan_tmp, &total);
+#pragma unroll
+  for (int i = 0; i < kBucketChunk; ++i)
+    if (i < P.nb) {
+      hist[P.b0 + i] = run;
+      run += P.c[i];
+    }
+  __syncthreads();
+  // experts: routed rows, padded segment starts
+  const bool owner = tid < E;  // E <= 1024: one expert per thread
+  int rows = 0, pstart = 0;
+  if (owner) {
+    pstart = hist[tid * NR];
+    rows = (tid + 1 < E ? hist[(tid + 1) * NR] : total) - pstart;
+  }
+  const int padded = (rows + BM - 1) / BM * BM;
+  int np;
+  const int seg0 = block_excl_scan(padded, sm.scan_tmp, &np);
+  if (owner) {
+    sm.seg0[tid] = seg0;
+    sm.rows[tid] = rows;
+    sm.p0[tid] = pstart;
+    if (tid == E - 1) sm.seg0[E] = np;
+  }
+  __syncthreads();
+  // padded bucket starts; LoRA segments and block tiles of the thread's buckets
+  int nseg = 0, ntile = 0;
+  const int e0 = P.b0 / NR, a0 = P.b0 - e0 * NR;  // (expert, rank) of the first bucket
+  {
+    int e = e0, a = a0;
+#pragma unroll
+    for (int i = 0; i < kBucketChunk; ++i) {
+      if (i < P.nb) {
+        const int b = P.b0 + i;
+        const int st = sm.seg0[e] + hist[b] - sm.p0[e];
+        hist[b] = st;
+        if (a < NA && P.c[i] > 0) {
+          ++nseg;
+          ntile += (st + P.c[i] - 1) / BM - st / BM + 1;
+        }
+      }
+      if (++a == NR) {
+        a = 0;
+        ++e;
+      }
     }
   }
   int2 tot;
-  const int2 off = block_excl_scan2(nseg_e, ntile_e, sm.scan_tmp2, &tot);  // ends with a barrier
+  const int2 off = block_excl_scan2(nseg, ntile, sm.scan_tmp2, &tot);
+  // each expert's first tile index, from the thread holding its first bucket
+  int ti = off.y;
+  {
+    int e = e0, a = a0;
+#pragma unroll
+    for (int i = 0; i < kBucketChunk; ++i) {
+      if (i < P.nb) {
+        const int b = P.b0 + i;
+        if (a == 0) sm.tile0[e] = ti;
+        if (a < NA && P.c[i] > 0) ti += (hist[b] + P.c[i] - 1) / BM - hist[b] / BM + 1;
+      }
+      if (++a == NR) {
+        a = 0;
+        ++e;
+      }
+    }
+  }
+  __syncthreads();
   P.seg_off = off.x;
   P.tile_off = off.y;
   P.n_seg = tot.x;
   P.n_tiles = tot.y;
+  P.num_padded = np;
   return P;
 }
 
@@ -306,34 +362,53 @@ __device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan
   const int tid = threadIdx.x;
   const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, R = s.R;
   const int *start = sm.hist;
-  if (tid < E) {
-    const int e = tid, seg0 = P.seg0, seg1 = P.seg0 + P.padded;
-    al.seg_start[e] = seg0;
-    int si = P.seg_off, ti = P.tile_off;
-    int b_next = seg0 / BM;  // first block of e whose first tile is not yet written
-    for (int a = 0; a < NA; ++a) {
-      const int b = e * NR + a, st = start[b];
-      const int c = start[b + 1] - st;
-      if (c > 0) {
-        reinterpret_cast<int4 *>(al.lora_seg)[si++] = make_int4(e, a, st, c);
+  const int np = P.num_padded;
+  // the thread's buckets: start and row count, LoRA segment and block tiles
+  int si = P.seg_off, ti = P.tile_off;
+  int be = P.b0 / NR, ba = P.b0 - be * NR;  // (expert, rank) of bucket b0 + i
+#pragma unroll
+  for (int i = 0; i < kBucketChunk; ++i) {
+    if (i < P.nb) {
+      const int b = P.b0 + i;
+      const int st = start[b], c = P.c[i];
+      al.bucket_base[b] = st;
+      al.bucket_cnt[b] = c;
+      if (ba < NA && c > 0) {
+        reinterpret_cast<int4 *>(al.lora_seg)[si++] = make_int4(be, ba, st, c);
         for (int blk = st / BM; blk <= (st + c - 1) / BM; ++blk) {
-          for (; b_next <= blk; ++b_next) al.block_tile_start[b_next] = ti;
           const int lo = max(st, blk * BM), hi = min(st + c, (blk + 1) * BM);
-          reinterpret_cast<int4 *>(al.tiles)[ti++] = make_int4(blk, a, lo - blk * BM, hi - lo);
+          reinterpret_cast<int4 *>(al.tiles)[ti++] = make_int4(blk, ba, lo - blk * BM, hi - lo);
         }
       }
     }
-    for (; b_next < seg1 / BM; ++b_next) al.block_tile_start[b_next] = ti;
-    for (int b = seg0 / BM; b < seg1 / BM; ++b) al.block_expert[b] = e;
+    if (++ba == NR) {
+      ba = 0;
+      ++be;
+    }
   }
-  const int NB = E * NR, np = P.num_padded;
-  // bucket tables: start and row count of every (expert, adapter rank) bucket
-  for (int b = tid; b < NB; b += kAlignThreads) {
-    const int e = b / NR, a = b - e * NR, st = start[b];
-    const int end = a + 1 < NR ? start[b + 1] : sm.seg0[e] + sm.rows[e];
-    al.bucket_base[b] = st;
-    al.bucket_cnt[b] = end - st;
+  // blocks: expert (the last one whose segment starts at or before the
+  // block; empty experts share their start with the next) and first tile
+  // (the expert's first tile plus its tiles in earlier blocks)
+  for (int b = tid; b < s.nblk; b += kAlignThreads) {
+    int e = -1, t = P.n_tiles;
+    if (b < np / BM) {
+      const int pos = b * BM;
+      int lo = 0, hi = E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sm.seg0[mid] <= pos) lo = mid; else hi = mid;
+      }
+      e = lo;
+      t = sm.tile0[e];
+      for (int a = 0; a < NA; ++a) {
+        const int st = start[e * NR + a], c = start[e * NR + a + 1] - st;
+        if (c > 0) t += max(0, min(b, (st + c - 1) / BM + 1) - st / BM);
+      }
+    }
+    al.block_expert[b] = e;
+    al.block_tile_start[b] = t;
   }
+  if (tid < E) al.seg_start[tid] = sm.seg0[tid];
   // padding sentinels: slot j < BM - 1 past the end of each expert's rows
   for (int i = tid; i < E * (BM - 1); i += kAlignThreads) {
     const int e = i / (BM - 1), j = i - e * (BM - 1);
@@ -342,14 +417,13 @@ __device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan
   }
   if (tid == 0) {
     al.seg_start[E] = np;
+    al.block_tile_start[s.nblk] = P.n_tiles;
     al.counts[0] = np;
     al.counts[1] = P.n_seg;
     al.counts[2] = P.n_tiles;
     al.counts[3] = 0;
   }
   for (int i = np + tid; i < s.cap; i += kAlignThreads) al.sorted_rows[i] = R;
-  for (int b = np / BM + tid; b < s.nblk; b += kAlignThreads) al.block_expert[b] = -1;
-  for (int b = np / BM + tid; b <= s.nblk; b += kAlignThreads) al.block_tile_start[b] = P.n_tiles;
   for (int i = P.n_seg + tid; i < s.max_seg; i += kAlignThreads)
     reinterpret_cast<int4 *>(al.lora_seg)[i] = make_int4(-1, -1, 0, 0);
   for (int i = P.n_tiles + tid; i < s.max_tiles; i += kAlignThreads)
