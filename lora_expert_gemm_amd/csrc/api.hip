@@ -32,6 +32,7 @@ struct moelora_plan_s {
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
   int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
   int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
+  bool rotate = true;      // streaming GEMMs: staggered slab walks for 4 KB-multiple weight rows
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -164,6 +165,7 @@ Layout make_layout(const moelora_desc &d, int T) {
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t elem_bytes(const moelora_desc &d) { return d.dtype == MOELORA_BF16 ? 2 : 4; }
 
 moelora_status check_desc(const moelora_desc *d) {
   if (!d) return MOELORA_ERR_INVALID_ARG;
@@ -265,6 +267,7 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_DOWN_ROWS")) p->down_rows = atoi(v) == 32 ? 32 : atoi(v) == 16 ? 16 : 0;
   if (const char *v = getenv("MOELORA_SLOTS")) p->slots = ring_slots_supported(atoi(v)) ? atoi(v) : 0;
+  if (const char *v = getenv("MOELORA_ROTATE")) p->rotate = atoi(v) != 0;
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -444,6 +447,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.z = z_gu;
     a.z2 = z2_gu;
     a.waves = waves_gu;
+    a.rotate = plan->rotate && (size_t)d.hidden * elem_bytes(d) % 4096 == 0;
     MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, true, vg, st) : launch_gate_up(a, vg, st));
   }
   MOELORA_TRY(mark());
@@ -464,6 +468,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.z = z_d;
     a.z2 = z2_d;
     a.waves = waves_d;
+    a.rotate = plan->rotate && (size_t)d.inter * elem_bytes(d) % 4096 == 0;
     if (row) {
       a.rs = RowShrinkArgs{h, lora_a_d, z_d, adapter_ids, d.inter, vd.vec};
       a.row_wgs = s.R;

@@ -151,18 +151,24 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
 // loaded straight into registers, one slab ahead.  Each slab issues the same
 // number of loads (past the end the last slab is fetched again into a free
 // slot), which makes a fixed vmcnt the wait for "slab j and its tokens".
-// Weight loads are marked non-temporal: each line is read once.
+// Weight loads are marked non-temporal: each line is read once.  rot
+// (0 <= rot < K / 64) starts the walk at slab rot and wraps around: with
+// row strides that are multiples of 4 KB, workgroups that walk the same
+// slab columns at once stream ~13 % slower than staggered ones.
 template <int NG, int NW, int S>
 __device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
                                              const uint16_t *const *xr, int K, int kg, int ri,
-                                             unsigned char *ring, f32x4_t *acc0, f32x4_t *acc1) {
+                                             int rot, unsigned char *ring, f32x4_t *acc0,
+                                             f32x4_t *acc1) {
   using M = Mma<uint16_t>;
   constexpr int kSlot = NW * 2048;
   constexpr int kYoung = 2 * NW + 2 * NG;  // loads issued after a slab's token loads
   static_assert(kYoung < 16, "vmcnt immediate");
   constexpr int kWait = 0x0f70 | kYoung;   // vmcnt(kYoung), expcnt / lgkmcnt unconstrained
   const int nsl = K / 64;
+  auto slab = [&](int j) { return j + rot >= nsl ? j + rot - nsl : j + rot; };
   auto dma = [&](int j, int p) {
+    j = slab(j);
     unsigned char *d = ring + p * kSlot;
 #pragma unroll
     for (int t = 0; t < NW; ++t)
@@ -176,6 +182,7 @@ __device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
     u32x4_t b[2][NG];
   };
   auto tload = [&](Tok &tk, int j) {
+    j = slab(j);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -222,14 +229,20 @@ __device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
 template <int TG, int NW, int S>
 __device__ __forceinline__ void contract_dma_groups(const uint16_t *const *dsrc,
                                                     const uint16_t *const *xr, int ntg, int K, int kg,
-                                                    int ri, unsigned char *ring, f32x4_t *acc0,
-                                                    f32x4_t *acc1) {
+                                                    int ri, int rot, unsigned char *ring,
+                                                    f32x4_t *acc0, f32x4_t *acc1) {
   if (TG >= 4 && ntg > 2)
-    contract_dma<TG, NW, S>(dsrc, xr, K, kg, ri, ring, acc0, acc1);
+    contract_dma<TG, NW, S>(dsrc, xr, K, kg, ri, rot, ring, acc0, acc1);
   else if (TG >= 2 && ntg > 1)
-    contract_dma<(TG >= 2 ? 2 : 1), NW, S>(dsrc, xr, K, kg, ri, ring, acc0, acc1);
+    contract_dma<(TG >= 2 ? 2 : 1), NW, S>(dsrc, xr, K, kg, ri, rot, ring, acc0, acc1);
   else
-    contract_dma<1, NW, S>(dsrc, xr, K, kg, ri, ring, acc0, acc1);
+    contract_dma<1, NW, S>(dsrc, xr, K, kg, ri, rot, ring, acc0, acc1);
+}
+
+// Starting slab of a workgroup's weight walk (contract_dma): staggered over
+// workgroups when a.rotate is set, else 0.
+__device__ __forceinline__ int walk_start(const GemmArgs &a, int K) {
+  return a.rotate ? (int)((blockIdx.x * 7u) % (unsigned)(K / 64)) : 0;
 }
 
 // z values of a lane's rows for the batched expand below: row mode, z of
@@ -469,7 +482,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
       dsrc[2 + i] = g + (size_t)I * H;
     }
     contract_dma_groups<TG, 2, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                  active_groups<TG>(a, blk), H, kg, ri, smem + wave * S * 4096, ag, au);
+                                  active_groups<TG>(a, blk), H, kg, ri, walk_start(a, H),
+                                  smem + wave * S * 4096, ag, au);
   } else {
     contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, active_groups<TG>(a, blk), H, kg, ag, au);
   }
@@ -572,8 +586,8 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
                      8 * ((lane & 7) ^ (r & 7));
       }
     contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                   active_groups<TG>(a, blk), I, kg, ri, smem + wave * S * NW * 2048,
-                                   acc, acc1);
+                                   active_groups<TG>(a, blk), I, kg, ri, walk_start(a, I),
+                                   smem + wave * S * NW * 2048, acc, acc1);
   } else {
     contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
   }

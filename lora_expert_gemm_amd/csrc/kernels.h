@@ -66,6 +66,8 @@ struct GemmArgs {
   int down_rows;           // streaming down GEMM: weight rows per wave (16, or 32 = two tiles)
   int slots;               // streaming GEMMs: LDS ring slots per wave for the weight stream
                            // (bf16, contraction a multiple of 64); 0: loads into registers
+  int rotate;              // LDS ring: workgroups start their contraction walk at staggered
+                           // slabs (weight rows a multiple of 4 KB), 0: all at slab 0
   int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
                            // result (tiled shrink -> 8-wave GEMM); zero_row: 64 bf16 zeros
   void *zero_row;

@@ -227,6 +227,39 @@ def test_weight_stream_paths_agree(T, H, I, E, k, NA, r, monkeypatch):
     assert np.array_equal(outs["0"], outs["4"])
 
 
+# Weight rows that are a multiple of 4 KB: the LDS-ring walks start at a
+# slab that depends on the workgroup (gate_up rows of 2048 bf16, then down
+# rows of 2048 bf16 with 32-row blocks).
+ROT = [
+    (8, 2048, 256, 4, 2, 2, 16),
+    (40, 256, 2048, 8, 2, 3, 16),
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r", ROT)
+def test_staggered_walks(T, H, I, E, k, NA, r, monkeypatch):
+    """Staggered and aligned slab walks each meet the oracle's tolerance and
+    agree with each other to within it (the contraction is summed in another
+    order); 3 and 4 ring slots walk the same order, so they agree bit for bit."""
+    w = synth.Workload("rot", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
+                       adapters="uniform_with_none", seed=T * 13 + H)
+    d = synth.make_inputs(w)
+    rid, rw = oracle.ref_route(d["logits"], k)
+    ref = oracle_out(w, d, rid, rw)
+    outs = {}
+    for rot in ("1", "0"):
+        monkeypatch.setenv("MOELORA_ROTATE", rot)
+        for slots in ("3", "4"):
+            monkeypatch.setenv("MOELORA_SLOTS", slots)
+            run = Run(w, d).forward()
+            say(f"[parity] rotate={rot} slots={slots} {w}: plan {run.plan.info(T)}")
+            outs[rot, slots] = run.out.cpu().numpy().copy()
+            check_close(run.out_f32(), ref, "bf16", f"rotate {rot} slots {slots}")
+        assert np.array_equal(outs[rot, "3"], outs[rot, "4"])
+    f32 = lambda o: synth.bf16_bits_to_f32(o.view(np.uint16))
+    check_close(f32(outs["1", "3"]), f32(outs["0", "3"]), "bf16", "staggered vs aligned")
+
+
 SAMPLES = {"tiny_fp32": 8, "decode_bf16": 16, "illustrative_bf16": 12,
            "prefill_bf16": 20, "many_expert_bf16": 48}
 
