@@ -143,8 +143,10 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
 // rows each (lane l: row l / 8, one 16-byte chunk), so every load
 // instruction covers whole 128-byte lines -- the register path above has a
 // lane per (row, chunk of a 64-byte half line) and streams slower.  Slabs go
-// round a per-wave ring of S slots in LDS with S - 1 of them in flight; the
-// MFMA operand of lane l (row l % 16, chunk l / 16 of a 32-wide step) is then
+// round a per-wave ring of S slots in LDS: step j fetches slab j + S - 1 and
+// the tokens of slab j + 1, then waits for slab j and its tokens, which (the
+// counter retiring in issue order) also lands slab j + 1, so slab j + S - 1
+// is in flight while slab j is computed; the MFMA operand of lane l (row l % 16, chunk l / 16 of a 32-wide step) is then
 // one ds_read_b128.  Chunk c of tile row r sits at chunk c ^ (r % 8) of its
 // LDS row, so the 16 rows read at one chunk spread over distinct banks.
 // Tokens (L2-resident, shared by every workgroup of the block) are still
