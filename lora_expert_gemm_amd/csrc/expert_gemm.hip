@@ -146,10 +146,10 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
 // round a per-wave ring of S slots in LDS: step j fetches slab j + S - 1 and
 // the tokens of slab j + 1, then waits for slab j and its tokens, which (the
 // counter retiring in issue order) also lands slab j + 1, so slab j + S - 1
-// is in flight while slab j is computed.  The slab read at step j was thus
-// waited for a whole step earlier; that margin is needed: a two-slot ring,
-// which reads a slab right after the wait that lands it, read stale LDS
-// (outputs off by 80 %), so S >= 3.  The MFMA operand of lane l (row l % 16, chunk l / 16 of a 32-wide step) is then
+// is in flight while slab j is computed.  A two-slot ring gave wrong
+// outputs (80 % off; the cause was not isolated -- there the slab read at
+// step j is landed by step j's own wait, here by step j - 1's), so S >= 3.
+// The MFMA operand of lane l (row l % 16, chunk l / 16 of a 32-wide step) is then
 // one ds_read_b128.  Chunk c of tile row r sits at chunk c ^ (r % 8) of its
 // LDS row, so the 16 rows read at one chunk spread over distinct banks.
 // Tokens (L2-resident, shared by every workgroup of the block) are still

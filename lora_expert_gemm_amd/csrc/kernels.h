@@ -79,7 +79,7 @@ struct GemmArgs {
 // LDS ring slots per wave of the streaming GEMMs' weight stream (bf16 with a
 // contraction that is a multiple of 64); the launchers hold instances for
 // the counts ring_slots_supported accepts, 0 meaning loads into registers
-// (at least 3 slots: each slab must land a step before it is read).
+// (at least 3: a two-slot ring gave wrong outputs).
 constexpr int kRingSlots = 3;
 inline bool ring_slots_supported(int s) { return s == 0 || s == 3 || s == 4; }
 
