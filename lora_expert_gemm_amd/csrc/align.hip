@@ -458,6 +458,9 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
   // Each thread takes kHistBatch rows per pass with all their id loads in
   // flight before the LDS atomics (a pass per row would pay the global load
   // latency once per row).
+  // Tokens per adapter rank: a wave adds each of its distinct ranks once
+  // (a prefill's tokens share a few adapters, and per-lane atomics on one
+  // LDS word serialize).
   constexpr int kHistBatch = 8;
   int err = 0;
   for (int t0 = tid; t0 < T; t0 += kHistBatch * kAlignThreads) {
@@ -468,13 +471,22 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
       ar[u] = t < T ? adapter_rank(aid, t, NA, err) : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u)
-      if (ar[u] >= 0) atomicAdd(&tok_cnt[ar[u]], 1);
-  }
-  for (int p0 = tid; p0 < R; p0 += kHistBatch * kAlignThreads) {
-    int key[kHistBatch];
-#pragma unroll
     for (int u = 0; u < kHistBatch; ++u) {
+      unsigned long long active = __ballot(ar[u] >= 0);
+      while (active) {
+        const int leader = __ffsll((long long)active) - 1;
+        const int key = __shfl(ar[u], leader);
+        const unsigned long long peers = __ballot(ar[u] == key) & active;
+        if (lane == leader) atomicAdd(&tok_cnt[key], __popcll(peers));
+        active &= ~peers;
+      }
+    }
+  }
+  constexpr int kRowBatch = 16;
+  for (int p0 = tid; p0 < R; p0 += kRowBatch * kAlignThreads) {
+    int key[kRowBatch];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
       const int p = p0 + u * kAlignThreads;
       key[u] = -1;
       if (p < R) {
@@ -486,7 +498,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
       }
     }
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u)
+    for (int u = 0; u < kRowBatch; ++u)
       if (key[u] >= 0) atomicAdd(&sm.hist[key[u]], 1);
   }
   if (err) atomicOr(&err_all, err);
