@@ -243,6 +243,7 @@ struct AlignSmem {
   int tile0[kMaxExperts];     // index of expert e's first LoRA tile
   int scan_tmp[kAlignWaves];
   int2 scan_tmp2[kAlignWaves];
+  int totals[3];              // align_plan_wave: padded rows, LoRA segments, tiles
 };
 
 // Everything that follows from the bucket histogram (in LDS): padded expert
@@ -354,6 +355,118 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
   P.n_seg = tot.x;
   P.n_tiles = tot.y;
   P.num_padded = np;
+  return P;
+}
+
+// Exclusive prefix sum over the 64 lanes of a wave; *total gets the sum.
+__device__ __forceinline__ int wave_excl_scan(int v, int *total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  *total = __shfl(x, kWave - 1);
+  return x - v;
+}
+
+// align_plan for few experts and buckets (E <= 64, E (NA + 1) <= 64
+// kBucketChunk): wave 0 alone runs the same three scans at wave level, so
+// the plan has one workgroup barrier instead of eight (a decode step's
+// 288 buckets: ~5 us of block scans otherwise).  Same results.
+__device__ __forceinline__ bool align_plan_wave_ok(const Shape &s) {
+  return s.E <= kWave && s.E * (s.NA + 1) <= kWave * kBucketChunk;
+}
+
+__device__ AlignPlan align_plan_wave(const Shape &s, AlignSmem &sm) {
+  const int tid = threadIdx.x;
+  const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, NB = E * NR;
+  int *hist = sm.hist;
+  AlignPlan P{};
+  if (tid < kWave) {
+    const int per = (NB + kWave - 1) / kWave;
+    P.b0 = min(tid * per, NB);
+    P.nb = min(per, NB - P.b0);
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kBucketChunk; ++i) {
+      P.c[i] = i < P.nb ? hist[P.b0 + i] : 0;
+      sum += P.c[i];
+    }
+    int total;
+    int run = wave_excl_scan(sum, &total);
+    // (a wave's LDS accesses complete in program order)
+#pragma unroll
+    for (int i = 0; i < kBucketChunk; ++i)
+      if (i < P.nb) {
+        hist[P.b0 + i] = run;
+        run += P.c[i];
+      }
+    int rows = 0, pstart = 0;
+    if (tid < E) {
+      pstart = hist[tid * NR];
+      rows = (tid + 1 < E ? hist[(tid + 1) * NR] : total) - pstart;
+    }
+    const int padded = (rows + BM - 1) / BM * BM;
+    int np;
+    const int seg0 = wave_excl_scan(padded, &np);
+    if (tid < E) {
+      sm.seg0[tid] = seg0;
+      sm.rows[tid] = rows;
+      sm.p0[tid] = pstart;
+    }
+    if (tid == 0) sm.seg0[E] = np;
+    int nseg = 0, ntile = 0;
+    const int e0 = P.b0 / NR, a0 = P.b0 - e0 * NR;
+    {
+      int e = e0, a = a0;
+#pragma unroll
+      for (int i = 0; i < kBucketChunk; ++i) {
+        if (i < P.nb) {
+          const int b = P.b0 + i;
+          const int st = sm.seg0[e] + hist[b] - sm.p0[e];
+          hist[b] = st;
+          if (a < NA && P.c[i] > 0) {
+            ++nseg;
+            ntile += (st + P.c[i] - 1) / BM - st / BM + 1;
+          }
+        }
+        if (++a == NR) {
+          a = 0;
+          ++e;
+        }
+      }
+    }
+    int n_seg, n_tiles;
+    P.seg_off = wave_excl_scan(nseg, &n_seg);
+    P.tile_off = wave_excl_scan(ntile, &n_tiles);
+    int ti = P.tile_off;
+    {
+      int e = e0, a = a0;
+#pragma unroll
+      for (int i = 0; i < kBucketChunk; ++i) {
+        if (i < P.nb) {
+          const int b = P.b0 + i;
+          if (a == 0) sm.tile0[e] = ti;
+          if (a < NA && P.c[i] > 0) ti += (hist[b] + P.c[i] - 1) / BM - hist[b] / BM + 1;
+        }
+        if (++a == NR) {
+          a = 0;
+          ++e;
+        }
+      }
+    }
+    if (tid == 0) {
+      sm.totals[0] = np;
+      sm.totals[1] = n_seg;
+      sm.totals[2] = n_tiles;
+    }
+  }
+  __syncthreads();
+  P.num_padded = sm.totals[0];
+  P.n_seg = sm.totals[1];
+  P.n_tiles = sm.totals[2];
   return P;
 }
 
@@ -504,7 +617,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
   if (err) atomicOr(&err_all, err);
   __syncthreads();
 
-  const AlignPlan P = align_plan(s, sm);
+  const AlignPlan P = align_plan_wave_ok(s) ? align_plan_wave(s, sm) : align_plan(s, sm);
   if (tid == 0) {
     int run = 0;
     for (int a = 0; a < NR; ++a) {
@@ -688,7 +801,8 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align_small(
   __syncthreads();
   if (tid < R) key[tid] = my_key;
 
-  const AlignPlan P = align_plan(s, sm);  // ends with a barrier: key[] visible
+  // ends with a barrier: key[] visible
+  const AlignPlan P = align_plan_wave_ok(s) ? align_plan_wave(s, sm) : align_plan(s, sm);
 
   // stable rank inside the bucket: earlier rows with the same key
   if (my_key >= 0) {
