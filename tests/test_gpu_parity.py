@@ -58,6 +58,9 @@ SMALL = [
     (8, 64, 96, 1024, 32, 7, 256, "bf16", "uniform_with_none"), # maximum E, top-k and rank (row mode)
     (64, 64, 64, 32, 2, 255, 8, "bf16", "uniform_with_none"),   # maximum adapters: 8192 alignment buckets
     (300, 64, 64, 64, 2, 3, 256, "bf16", "uniform_with_none"),  # rank 256 in tile mode (split shrink)
+    (100, 64, 64, 64, 2, 8, 16, "bf16", "uniform_with_none"),   # 576 buckets: one-wave alignment plan, 9 per lane
+    (100, 64, 64, 64, 2, 9, 16, "bf16", "uniform_with_none"),   # 640 buckets: block-wide alignment plan
+    (40, 64, 64, 65, 2, 2, 16, "bf16", "uniform_with_none"),    # 65 experts: block-wide plan in the small kernel
 ]
 
 
