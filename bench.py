@@ -90,6 +90,13 @@ def measured_traffic(workload, stage):
     return v["bytes"] if v else None
 
 
+def hbm_bound(alg, stage, dtype):
+    """Whether a stage is bound by HBM: its algorithmic FLOPs per byte below
+    the ridge point (peak FLOP/s over peak bytes/s of the dtype's MFMA)."""
+    ridge = MFMA_PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return alg[f"{stage}_flop"] < ridge * alg[f"{stage}_bytes"]
+
+
 def algorithmic(w, ids, aid, row_mode=False):
     """Bytes and FLOPs the method must move / compute for one call: weights of
     the experts and (adapter, expert) pairs routed to, x read, out written;
@@ -300,9 +307,9 @@ def main():
     alg = algorithmic(w, ids, d["adapter_ids"] if not args.no_lora
                       else np.full(w.T, -1, np.int32), "lora_mode=row" in plan.info(w.T))
 
-    decode = w.T * w.k <= 24 * w.E
     dom = max(("gate_up", "down"), key=lambda n: stage[n])
     dom_s = stage[dom] / 1e3
+    decode = hbm_bound(alg, dom, w.dtype)
     if decode:
         roof = {"bound": "hbm", "kernel": dom, "achieved": alg[f"{dom}_bytes"] / dom_s / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}

@@ -66,12 +66,18 @@ int choose_tg(const moelora_desc &d, int T) {
   // Streaming blocks: 16 rows while experts average at most 4 rows, then 32
   // rows (most experts' rows in one block, so their weights stream once,
   // without the register cost of 64-row blocks).
-  if (tiled_ok(d) && rows >= 64 * ne) return kTgTiled;
   // tuning sweeps only: force the streaming block size (1, 2 or 4 groups of 16)
   if (const char *v = getenv("MOELORA_TG")) {
     const int tg = atoi(v);
     if (tg == 1 || tg == 2 || tg == 4) return tg;
   }
+  // One expert (a dense layer) at decode size: the grid is one or two blocks
+  // wide, so the 128-row tiled kernel (43 workgroups for a 64-token step of
+  // the 4096 x 11008 MLP: 698 us) and 64-row blocks (274 us) leave most CUs
+  // idle; 32-row blocks stream each weight once per block but fill the chip
+  // (185 us).
+  if (d.n_experts == 1 && rows <= 128) return kTgMid;
+  if (tiled_ok(d) && rows >= 64 * ne) return kTgTiled;
   if (rows <= 4 * ne) return kTgSmall;
   if (rows <= 32 * ne) return kTgMid;
   return kTgLarge;
@@ -86,9 +92,12 @@ int choose_tg(const moelora_desc &d, int T) {
 // when the intermediate size is large (4 % ahead at 11008 columns) and of
 // one wave otherwise (8 % ahead at 768 columns, where a block has only 48
 // column tiles).
-int choose_waves(int tg, bool gate_up, int inter) {
+int choose_waves(int tg, bool gate_up, int inter, long long ne) {
   if (tg == kTgSmall) return 4;
-  if (tg == kTgMid) return gate_up ? (inter >= 4096 ? 4 : 1) : 2;
+  // (with one or two experts the block count is too small for 4-wave
+  // gate_up workgroups to spread evenly over the CUs: 143 -> 92 us with
+  // one-wave workgroups for the dense 64-token step)
+  if (tg == kTgMid) return gate_up ? (inter >= 4096 && ne > 2 ? 4 : 1) : 2;
   return 4;
 }
 int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
@@ -127,8 +136,9 @@ Layout make_layout(const moelora_desc &d, int T) {
   s.max_seg = (int)std::min<long long>(s.R, (long long)s.E * s.NA);
   s.max_tiles = s.nblk + s.max_seg;
   const int tg = s.BM / 16;
-  L.waves_gu = choose_waves(tg, true, d.inter);
-  L.waves_d = choose_waves(tg, false, d.inter);
+  const long long ne_used = std::max<long long>(1, std::min<long long>(d.n_experts, s.R));
+  L.waves_gu = choose_waves(tg, true, d.inter, ne_used);
+  L.waves_d = choose_waves(tg, false, d.inter, ne_used);
   L.split = choose_split(tg, s.R);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
   const size_t NB = (size_t)s.E * (s.NA + 1);

@@ -62,6 +62,10 @@ WORKLOADS = [
     Workload("many_expert_bf16", T=256, H=2048, I=768, E=128, k=8, NA=32,
              r=16, dtype="bf16", adapters="zipf_with_none", bias_var=0.5,
              seed=1004),
+    # dense (non-MoE) multi-LoRA: one expert, top-1, on the illustrative
+    # shape (the post's Figure 1 MLP); not one of the five reference configs
+    Workload("dense_bf16", T=64, H=4096, I=11008, E=1, k=1, NA=16, r=32,
+             dtype="bf16", adapters="uniform_with_none", seed=1005),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 

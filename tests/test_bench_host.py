@@ -100,3 +100,18 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr and p.stdout == ""
+
+
+def test_roofline_bound_follows_the_ridge_point():
+    # bf16 ridge: 2500 TFLOP/s / 8000 GB/s = 312.5 FLOP per byte
+    assert bench.hbm_bound({"gate_up_flop": 312.0, "gate_up_bytes": 1.0}, "gate_up", "bf16")
+    assert not bench.hbm_bound({"gate_up_flop": 313.0, "gate_up_bytes": 1.0}, "gate_up", "bf16")
+    # the five workloads' gate_up by hand: decode-sized steps stream, prefill computes
+    w = synth.workload("decode_bf16")
+    rows = w.T * w.k
+    flop, byts = 2.0 * rows * 2 * w.I * w.H, 2.0 * 26 * 2 * w.I * w.H
+    assert bench.hbm_bound({"d_flop": flop, "d_bytes": byts}, "d", "bf16")
+    w = synth.workload("prefill_bf16")
+    rows = w.T * w.k
+    flop, byts = 2.0 * rows * 2 * w.I * w.H, 2.0 * w.E * 2 * w.I * w.H + 2.0 * w.T * w.H
+    assert not bench.hbm_bound({"p_flop": flop, "p_bytes": byts}, "p", "bf16")

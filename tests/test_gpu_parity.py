@@ -61,6 +61,9 @@ SMALL = [
     (100, 64, 64, 64, 2, 8, 16, "bf16", "uniform_with_none"),   # 576 buckets: one-wave alignment plan, 9 per lane
     (100, 64, 64, 64, 2, 9, 16, "bf16", "uniform_with_none"),   # 640 buckets: block-wide alignment plan
     (40, 64, 64, 65, 2, 2, 16, "bf16", "uniform_with_none"),    # 65 experts: block-wide plan in the small kernel
+    (24, 256, 384, 1, 1, 3, 16, "bf16", "uniform_with_none"),   # dense: one expert, top-1, row-wise LoRA
+    (300, 256, 384, 1, 1, 3, 16, "bf16", "uniform_with_none"),  # dense, LDS-tiled 128-row blocks
+    (20, 96, 160, 1, 1, 2, 8, "f32", "uniform_with_none"),      # dense, float
 ]
 
 
@@ -264,7 +267,7 @@ def test_staggered_walks(T, H, I, E, k, NA, r, monkeypatch):
 
 
 SAMPLES = {"tiny_fp32": 8, "decode_bf16": 16, "illustrative_bf16": 12,
-           "prefill_bf16": 20, "many_expert_bf16": 48}
+           "prefill_bf16": 20, "many_expert_bf16": 48, "dense_bf16": 8}
 
 
 @pytest.mark.parametrize("name", [w.name for w in synth.WORKLOADS])
