@@ -102,6 +102,32 @@ int choose_waves(int tg, bool gate_up, int inter, long long ne) {
 }
 int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
 
+// Contraction splits of the streaming down GEMM (bf16 weight stream through
+// the LDS ring).  When the (block, column tile) grid fills under a quarter
+// of the chip's workgroup slots -- a dense layer at decode size has one or
+// two blocks, i.e. 128 two-wave workgroups for 1536 slots -- the
+// contraction is split until it fills them (at most 8 splits of at least 16
+// slabs), each split writing its own partial y, which the combine adds in
+// split order.  At a third of the slots (the illustrative decode step) the
+// split measured 0-9 % slower, hence the quarter.
+constexpr int kComputeUnits = 256;  // MI355X
+int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d) {
+  if (tg == kTgTiled || d.dtype != MOELORA_BF16 || d.inter % 64 != 0) return 1;
+  // tuning sweeps only: force the split count (1..8; every split keeps a slab)
+  if (const char *v = getenv("MOELORA_KSPLIT_D")) {
+    const int k = atoi(v);
+    if (k >= 1 && k <= 8) return std::max(1, std::min(k, d.inter / 64));
+  }
+  const int nw = choose_down_rows(tg) == 32 ? 2 : 1;  // 16-row weight tiles per wave
+  const long long slots = (long long)kComputeUnits * std::max(1, 160 * 1024 / (kRingSlots * nw * 2048 * waves_d));
+  const int cols = 16 * nw * waves_d;
+  const long long grid = (long long)((s.H + cols - 1) / cols) *
+                         std::max<long long>(std::min(s.E, s.R), (s.R + s.BM - 1) / s.BM);
+  if (4 * grid > slots) return 1;
+  const long long k = std::min<long long>({slots / std::max<long long>(1, grid), 8, d.inter / 64 / 16});
+  return (int)std::max<long long>(1, k);
+}
+
 // Workgroups sharing one shrink tile's contraction: a decode step has only
 // tens of LoRA tiles, so each is split over several CUs.
 int choose_split(int tg, int R) {
@@ -111,7 +137,7 @@ int choose_split(int tg, int R) {
 
 struct Layout {
   Shape s;
-  int waves_gu, waves_d, split;
+  int waves_gu, waves_d, split, ksplit;
   size_t off_error, off_counts, off_ids, off_w, off_sorted, off_bexp, off_seg, off_lseg,
       off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_rpos, off_zero, off_zgu,
       off_zd, off_h, off_y, total;
@@ -139,6 +165,13 @@ Layout make_layout(const moelora_desc &d, int T) {
   const long long ne_used = std::max<long long>(1, std::min<long long>(d.n_experts, s.R));
   L.waves_gu = choose_waves(tg, true, d.inter, ne_used);
   L.waves_d = choose_waves(tg, false, d.inter, ne_used);
+  L.ksplit = choose_ksplit(d, s, tg, L.waves_d);
+  if (L.ksplit > 1 && L.waves_d != 4) {
+    // split down GEMMs run with four-wave workgroups (the dense 64-token
+    // step: 71 -> 56 us with 8 splits)
+    L.waves_d = 4;
+    L.ksplit = choose_ksplit(d, s, tg, L.waves_d);
+  }
   L.split = choose_split(tg, s.R);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
   const size_t NB = (size_t)s.E * (s.NA + 1);
@@ -169,7 +202,7 @@ Layout make_layout(const moelora_desc &d, int T) {
   L.off_zgu = take(4ull * L.split * s.cap * s.r);
   L.off_zd = take(4ull * L.split * s.cap * s.r);
   L.off_h = take(es * s.cap * s.I);
-  L.off_y = take(4ull * s.R * s.H);
+  L.off_y = take(4ull * L.ksplit * s.R * s.H);
   L.total = o;
   return L;
 }
@@ -324,14 +357,18 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   const int wgu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
   const int wd = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
   const int down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
+  const int ksplit = vd.bf16 && vd.vec && vd.even_k && d.inter % 64 == 0 && plan->slots != 0 &&
+                             tg != kTgTiled
+                         ? L.ksplit
+                         : 1;
   snprintf(buf, buf_len,
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
-           "k_tail_d=%d waves_gu=%d waves_d=%d down_rows=%d lora_mode=%s shrink_split=%d cap=%d "
-           "workspace=%zu",
+           "k_tail_d=%d waves_gu=%d waves_d=%d down_rows=%d down_ksplit=%d lora_mode=%s "
+           "shrink_split=%d cap=%d workspace=%zu",
            vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
            k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, tg == kTgTiled ? 0 : down_rows,
-           d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile", L.split,
-           L.s.cap, L.total);
+           ksplit, d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile",
+           L.split, L.s.cap, L.total);
   return MOELORA_OK;
 }
 
@@ -430,6 +467,12 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   g.split = L.split;
   g.down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
   g.slots = plan->slots;
+  // contraction splits of the down GEMM: only where its weight stream goes
+  // through the LDS ring
+  g.ksplit = vd.bf16 && vd.vec && vd.even_k && d.inter % 64 == 0 && plan->slots != 0 &&
+                     tg != kTgTiled
+                 ? L.ksplit
+                 : 1;
   g.zero_row = ws + L.off_zero;
   const bool t8 = tg == kTgTiled;
   const int z2_gu = lora && t8 && fused_lora_ok(d, d.hidden);
@@ -486,7 +529,8 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, false, vd, st) : launch_down(a, vd, st));
   }
   MOELORA_TRY(mark());
-  MOELORA_TRY(launch_combine(s, ids, wts, g.y, out, d.dtype == MOELORA_BF16, row ? z_d : nullptr,
+  MOELORA_TRY(launch_combine(s, ids, wts, g.y, g.ksplit, out, d.dtype == MOELORA_BF16,
+                             row ? z_d : nullptr,
                              lora_b_d, adapter_ids, vd.vec, st));
   MOELORA_TRY(mark());
 #undef MOELORA_TRY

@@ -522,7 +522,9 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
 // (float).  MODE 2 (row-wise LoRA): the first a.row_wgs workgroups compute
 // the down shrink of one routed row each, z_d[p] = h[pos_p] . A_d[a][e]^T,
 // alongside the base GEMM (both only need h); the expand then happens in
-// the combine.
+// the combine.  With a.ksplit > 1 (LDS ring only) the contraction is split
+// over workgroups: split q sums its slab range into y[q] (the expand goes to
+// split 0), and the combine adds the partials in split order.
 template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2, int S>
 __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   constexpr int BM = 16 * TG;
@@ -548,9 +550,20 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   const int blk = gt.blk;
   const int e = a.al.block_expert[blk];
   const int I = s.I, H = s.H;
+  // column tile and contraction split: the tiles of split q follow those of
+  // split q - 1; split q takes slabs [q nsl / ksplit, (q + 1) nsl / ksplit)
+  const int cols = (R2 ? 32 : 16) * a.waves;
+  const int ntn = (H + cols - 1) / cols;
+  const int ksp = gt.nt / ntn, nt = gt.nt - ksp * ntn;
+  int k0 = 0, kn = I;
+  if (S > 0 && a.ksplit > 1) {
+    const int nsl = I / 64;
+    k0 = 64 * (ksp * nsl / a.ksplit);
+    kn = 64 * ((ksp + 1) * nsl / a.ksplit) - k0;
+  }
   // R2: the wave owns two 16-row tiles (rows m0 .. m0+31), two weight
   // streams against one set of h fragments
-  const int m0 = (gt.nt * a.waves + wave) * (R2 ? 32 : 16);
+  const int m0 = (nt * a.waves + wave) * (R2 ? 32 : 16);
   if (e < 0 || m0 >= H) return;
   const int mrow = min(m0 + ri, H - 1);
   const int mrow1 = R2 ? min(m0 + 16 + ri, H - 1) : mrow;
@@ -566,7 +579,7 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
     // padding rows read the block's first row (always a routed row): the
     // same lines as a real lane, so they coalesce instead of fetching
     // unwritten rows of h
-    xr[tg] = static_cast<const DT *>(a.h) + ((size_t)blk * BM + (ok[tg] ? tg * 16 + ri : 0)) * I;
+    xr[tg] = static_cast<const DT *>(a.h) + ((size_t)blk * BM + (ok[tg] ? tg * 16 + ri : 0)) * I + k0;
   }
   int t0 = 0, t1 = 0;
   ZRows<DT, TG> zr{};
@@ -588,15 +601,15 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
       for (int i = 0; i < 2; ++i) {
         const int r = 16 * t + 8 * i + (lane >> 3);
         dsrc[2 * t + i] = static_cast<const uint16_t *>(a.W) + ((size_t)e * H + min(m0 + r, H - 1)) * I +
-                     8 * ((lane & 7) ^ (r & 7));
+                          k0 + 8 * ((lane & 7) ^ (r & 7));
       }
     contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                   active_groups<TG>(a, blk), I, kg, ri, walk_start(a, I),
+                                   active_groups<TG>(a, blk), kn, kg, ri, walk_start(a, kn),
                                    smem + wave * S * NW * 2048, acc, acc1);
   } else {
     contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
   }
-  if (MODE == 1)
+  if (MODE == 1 && ksp == 0)
     expand<DT, TG, VEC, R2, false>(a, blk, e, t0, t1, zr, static_cast<const DT *>(a.B), (size_t)H,
                                    mrow, (size_t)(mrow1 - mrow), kg, ri, prow, acc, acc1);
 #pragma unroll
@@ -606,7 +619,7 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
     for (int tg = 0; tg < TG; ++tg) {
       if (!ok[tg]) continue;
       const f32x4_t v4 = half ? acc1[tg] : acc[tg];
-      float *dst = a.y + (size_t)prow[tg] * H + mb;
+      float *dst = a.y + ((size_t)ksp * s.R + prow[tg]) * H + mb;
       if (VEC && mb + 3 < H) {
         *reinterpret_cast<float4 *>(dst) = make_float4(v4[0], v4[1], v4[2], v4[3]);
       } else {
@@ -716,14 +729,16 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
 }
 
 // out[t] = sum_j w[t][j] * y[t*k + j] in ascending j (float), rounded to
-// the layer dtype; rows with an out-of-range expert id add nothing.  With
+// the layer dtype, where y[p] = y[0][p] + y[1][p] + ... over the down
+// GEMM's ksplit contraction partials, in order; rows with an out-of-range
+// expert id add nothing.  With
 // z_d (row-wise LoRA), each row first gets its down expand added:
 // y[p][m] += sum_c z_d[p][c] B_d[a][e][m][c] (the expand is linear, so it
 // may follow the base GEMM in a later kernel).
 template <typename DT, bool VEC>
 __global__ __launch_bounds__(256) void k_combine(Shape s, const int *__restrict__ ids,
                                                  const float *__restrict__ w,
-                                                 const float *__restrict__ y, DT *out,
+                                                 const float *__restrict__ y, int ksplit, DT *out,
                                                  const float *__restrict__ z_d,
                                                  const DT *__restrict__ B_d,
                                                  const int *__restrict__ aid) {
@@ -738,15 +753,27 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, const int *__restrict_
     if (e < 0 || e >= s.E) continue;
     const float wj = w[p];
     const float *yr = y + (size_t)p * H + m0;
+    const size_t ys = (size_t)s.R * H;  // stride of the contraction partials
     if (VEC) {
-      const float4 v4 = *reinterpret_cast<const float4 *>(yr);
+      float4 v4 = *reinterpret_cast<const float4 *>(yr);
+      for (int q = 1; q < ksplit; ++q) {
+        const float4 u4 = *reinterpret_cast<const float4 *>(yr + q * ys);
+        v4.x += u4.x;
+        v4.y += u4.y;
+        v4.z += u4.z;
+        v4.w += u4.w;
+      }
       acc[0] += wj * v4.x;
       acc[1] += wj * v4.y;
       acc[2] += wj * v4.z;
       acc[3] += wj * v4.w;
     } else {
       for (int q = 0; q < 4; ++q)
-        if (m0 + q < H) acc[q] += wj * yr[q];
+        if (m0 + q < H) {
+          float v = yr[q];
+          for (int u = 1; u < ksplit; ++u) v += yr[u * ys + q];
+          acc[q] += wj * v;
+        }
     }
   }
   DT *o = out + (size_t)t * H + m0;
@@ -765,7 +792,8 @@ constexpr int kRankChunks = 4;  // up-front B chunk loads of the row-wise combin
 template <typename DT, bool VEC, int KB>
 __global__ __launch_bounds__(64) void k_combine_rows(Shape s, const int *__restrict__ ids,
                                                      const float *__restrict__ w,
-                                                     const float *__restrict__ y, DT *out,
+                                                     const float *__restrict__ y, int ksplit,
+                                                     DT *out,
                                                      const float *__restrict__ z_d,
                                                      const DT *__restrict__ B_d,
                                                      const int *__restrict__ aid) {
@@ -790,6 +818,7 @@ __global__ __launch_bounds__(64) void k_combine_rows(Shape s, const int *__restr
       ok[u] = j0 + u < s.k && e >= 0 && e < s.E;
       const int ee = ok[u] ? e : 0, pp = ok[u] ? p : t * s.k;
       v[u] = y[(size_t)pp * H + m];
+      for (int q = 1; q < ksplit; ++q) v[u] += y[((size_t)q * s.R + pp) * H + m];
       wt[u] = w[pp];
       b[u] = B_d + (((size_t)ad * s.E + ee) * H + m) * r;
       zp[u] = z_d + (size_t)pp * r;
@@ -883,7 +912,8 @@ hipError_t launch_d(const GemmArgs &a, int ntn, hipStream_t st) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(extra + ntn * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
+  const int ks = S > 0 ? a.ksplit : 1;
+  hipLaunchKernelGGL(kern, dim3(extra + ntn * ks * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
   return hipGetLastError();
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2>
@@ -968,14 +998,14 @@ hipError_t launch_shrink(const GemmArgs &a, const GemmVariant &v, bool from_h, h
   MOELORA_SHRINK(v, false);
 }
 
-hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const float *y,
+hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const float *y, int ksplit,
                           void *out, bool bf16, const float *z_d, const void *B_d,
                           const int *adapter_ids, bool vec, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   if (z_d) {
     const dim3 grid(s.T, (s.H + 63) / 64);
 #define MOELORA_COMB(DT, V, KB)                                                                \
-  hipLaunchKernelGGL((k_combine_rows<DT, V, KB>), grid, dim3(64), 0, st, s, ids, w, y,         \
+  hipLaunchKernelGGL((k_combine_rows<DT, V, KB>), grid, dim3(64), 0, st, s, ids, w, y, ksplit, \
                      static_cast<DT *>(out), z_d, static_cast<const DT *>(B_d), adapter_ids)
 #define MOELORA_COMB_K(DT, V)                                                                  \
   do {                                                                                         \
@@ -994,7 +1024,7 @@ hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const 
   }
   const dim3 grid(s.T, (s.H + 1023) / 1024);
 #define MOELORA_COMB(DT, V)                                                                    \
-  hipLaunchKernelGGL((k_combine<DT, V>), grid, dim3(256), 0, st, s, ids, w, y,                 \
+  hipLaunchKernelGGL((k_combine<DT, V>), grid, dim3(256), 0, st, s, ids, w, y, ksplit,         \
                      static_cast<DT *>(out), nullptr, nullptr, nullptr)
   const bool v4 = s.H % 4 == 0;
   if (bf16) {

@@ -66,13 +66,15 @@ struct GemmArgs {
   int down_rows;           // streaming down GEMM: weight rows per wave (16, or 32 = two tiles)
   int slots;               // streaming GEMMs: LDS ring slots per wave for the weight stream
                            // (bf16, contraction a multiple of 64); 0: loads into registers
+  int ksplit;              // streaming down GEMM with the LDS ring: contraction splits, each
+                           // writing its own partial y (1: none)
   int rotate;              // LDS ring: workgroups start their contraction walk at staggered
                            // slabs (weight rows a multiple of 4 KB), 0: all at slab 0
   int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
                            // result (tiled shrink -> 8-wave GEMM); zero_row: 64 bf16 zeros
   void *zero_row;
   void *h;                 // [cap][I] SiLU(gate)*up, layer dtype
-  float *y;                // [R][H] down output per routed row
+  float *y;                // [ksplit][R][H] down output per routed row (partials)
   AlignBufs al;
 };
 
@@ -118,8 +120,9 @@ hipError_t launch_tiled_shrink(const GemmArgs &a, bool from_h, hipStream_t st);
 hipError_t launch_down(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
 // Shrink of every LoRA tile (partial sums of a.split contraction splits).
 hipError_t launch_shrink(const GemmArgs &a, const GemmVariant &v, bool from_h, hipStream_t st);
-// out[t] = sum_j w[t][j] * (y[p] + [row mode] z_d[p] . B_d[a][e]^T), p = t*k + j.
-hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const float *y,
+// out[t] = sum_j w[t][j] * (y[p] + [row mode] z_d[p] . B_d[a][e]^T), p = t*k + j,
+// where y[p] is the sum of the ksplit partials y[0][p] + y[1][p] + ... in order.
+hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const float *y, int ksplit,
                           void *out, bool bf16, const float *z_d, const void *B_d,
                           const int *adapter_ids, bool vec, hipStream_t st);
 

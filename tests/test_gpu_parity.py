@@ -266,6 +266,40 @@ def test_staggered_walks(T, H, I, E, k, NA, r, monkeypatch):
     check_close(f32(outs["1", "3"]), f32(outs["0", "3"]), "bf16", "staggered vs aligned")
 
 
+# Down GEMM with its contraction split over workgroups (partial y per split,
+# added in split order by the combine): row-wise LoRA (small batch, expand in
+# the combine), tile-wise LoRA (64-row blocks, expand in split 0 only) and a
+# dense layer (one expert, top-1).
+KSPLIT = [
+    (24, 256, 256, 4, 2, 3, 16),    # 32-row blocks, row-wise LoRA
+    (160, 128, 256, 8, 2, 3, 16),   # 64-row blocks, tile-wise LoRA
+    (40, 128, 512, 1, 1, 3, 16),    # dense
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r", KSPLIT)
+def test_down_contraction_splits(T, H, I, E, k, NA, r, monkeypatch):
+    """1, 2 and 4 contraction splits of the down GEMM each meet the oracle's
+    tolerance and agree with each other to within it (the split sums round
+    differently, so not bit for bit)."""
+    w = synth.Workload("ksplit", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
+                       adapters="uniform_with_none", seed=T * 7 + I)
+    d = synth.make_inputs(w)
+    rid, rw = oracle.ref_route(d["logits"], k)
+    ref = oracle_out(w, d, rid, rw)
+    outs = {}
+    for ks in ("1", "2", "4"):
+        monkeypatch.setenv("MOELORA_KSPLIT_D", ks)
+        run = Run(w, d).forward()
+        info = run.plan.info(T)
+        say(f"[parity] down ksplit={ks} {w}: plan {info}")
+        assert f"down_ksplit={ks}" in info
+        outs[ks] = run.out_f32()
+        check_close(outs[ks], ref, "bf16", f"ksplit {ks}")
+    check_close(outs["2"], outs["1"], "bf16", "ksplit 2 vs 1")
+    check_close(outs["4"], outs["1"], "bf16", "ksplit 4 vs 1")
+
+
 SAMPLES = {"tiny_fp32": 8, "decode_bf16": 16, "illustrative_bf16": 12,
            "prefill_bf16": 20, "many_expert_bf16": 48, "dense_bf16": 8}
 
