@@ -33,6 +33,7 @@ struct moelora_plan_s {
   int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
   int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
   bool rotate = true;      // streaming GEMMs: staggered slab walks for 4 KB-multiple weight rows
+  int shrink_waves = 0;    // waves per shrink workgroup (0: by tile count)
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -133,6 +134,15 @@ int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d) {
 int choose_split(int tg, int R) {
   if (tg != kTgSmall) return 1;
   return std::max(1, std::min(8, 512 / std::max(R, 1)));
+}
+
+// Waves per shrink workgroup: 16 while the (tile, split) grid fits in two
+// such workgroups per CU, so each of a decode step's few tiles spreads over
+// a whole CU; 8 beyond (many experts of a few rows each: ~700 live tiles of
+// a 2236-workgroup grid, gate_up shrink 24 -> 19 us and down shrink 16 ->
+// 12 us; 4 waves measured between the two).
+int choose_shrink_waves(const Shape &s, int split) {
+  return (long long)s.max_tiles * split > 2 * kComputeUnits ? 8 : kShrinkWaves;
 }
 
 struct Layout {
@@ -311,6 +321,8 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   if (const char *v = getenv("MOELORA_DOWN_ROWS")) p->down_rows = atoi(v) == 32 ? 32 : atoi(v) == 16 ? 16 : 0;
   if (const char *v = getenv("MOELORA_SLOTS")) p->slots = ring_slots_supported(atoi(v)) ? atoi(v) : 0;
   if (const char *v = getenv("MOELORA_ROTATE")) p->rotate = atoi(v) != 0;
+  if (const char *v = getenv("MOELORA_SHRINK_WAVES"))
+    p->shrink_waves = atoi(v) == 4 || atoi(v) == 8 || atoi(v) == kShrinkWaves ? atoi(v) : 0;
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -364,11 +376,12 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   snprintf(buf, buf_len,
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
            "k_tail_d=%d waves_gu=%d waves_d=%d down_rows=%d down_ksplit=%d lora_mode=%s "
-           "shrink_split=%d cap=%d workspace=%zu",
+           "shrink_split=%d shrink_waves=%d cap=%d workspace=%zu",
            vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
            k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, tg == kTgTiled ? 0 : down_rows,
            ksplit, d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile",
-           L.split, L.s.cap, L.total);
+           L.split, plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(L.s, L.split),
+           L.s.cap, L.total);
   return MOELORA_OK;
 }
 
@@ -465,6 +478,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   GemmArgs g{};
   g.s = s;
   g.split = L.split;
+  g.shrink_waves = plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(s, L.split);
   g.down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
   g.slots = plan->slots;
   // contraction splits of the down GEMM: only where its weight stream goes

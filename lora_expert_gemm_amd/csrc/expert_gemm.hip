@@ -641,15 +641,15 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
 // result of split s goes to z_out[s][pos][c]; the expand that consumes z
 // adds the splits in split order: no atomics, no scheduling-dependent
 // rounding.
-template <typename DT, int TG, bool VEC, bool EVEN_K, bool FROM_H>
-__global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
+template <typename DT, int TG, bool VEC, bool EVEN_K, bool FROM_H, int NWV>
+__global__ __launch_bounds__(NWV * kWave) void k_shrink(GemmArgs a) {
   using M = Mma<DT>;
   constexpr int EPC = Elem<DT>::kPerChunk;
   constexpr int KS = M::kK;
   constexpr int BM = 16 * TG;
   // partial sums of the split contraction: [nks][16 * ntg rows][r], at most
-  // kShrinkWaves * 16 * 16 floats (r <= 16 * ncg and nks * ncg * ntg <= waves)
-  __shared__ float part[kShrinkWaves * 16 * 16];
+  // NWV * 16 * 16 floats (r <= 16 * ncg and nks * ncg * ntg <= NWV)
+  __shared__ float part[NWV * 16 * 16];
   const Shape &s = a.s;
   const int tile = blockIdx.x, split = blockIdx.y;
   if (tile >= a.al.counts[2]) return;
@@ -663,14 +663,14 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
   const int ncg = (r + 15) / 16;
   const int tg_lo = lo / 16, tg_hi = (lo + n - 1) / 16, ntg = tg_hi - tg_lo + 1;
   const int pairs = ncg * ntg;
-  const int nks = pairs >= kShrinkWaves ? 1 : kShrinkWaves / pairs;
+  const int nks = pairs >= NWV ? 1 : NWV / pairs;
   const int nsteps_all = (K + KS - 1) / KS;
   const int split_beg = (int)((long long)split * nsteps_all / a.split);
   const int split_end = (int)((long long)(split + 1) * nsteps_all / a.split);
   const int nsteps = split_end - split_beg;
   float *dst = a.z_out + (size_t)split * s.cap * r;
 
-  for (int u = wave; u < pairs * nks; u += kShrinkWaves) {
+  for (int u = wave; u < pairs * nks; u += NWV) {
     const int cg = u % ncg, tg = tg_lo + (u / ncg) % ntg, ks = u / pairs;
     const int s_beg = split_beg + (int)((long long)ks * nsteps / nks);
     const int s_end = split_beg + (int)((long long)(ks + 1) * nsteps / nks);
@@ -718,7 +718,7 @@ __global__ __launch_bounds__(kShrinkWaves * kWave) void k_shrink(GemmArgs a) {
   }
   if (nks == 1) return;
   __syncthreads();
-  for (int i = threadIdx.x; i < 16 * ntg * r; i += kShrinkWaves * kWave) {
+  for (int i = threadIdx.x; i < 16 * ntg * r; i += NWV * kWave) {
     const int row = i / r, c = i % r;
     const int local = tg_lo * 16 + row;
     if (local < lo || local >= lo + n) continue;
@@ -936,8 +936,15 @@ hipError_t go_down(const GemmArgs &a, hipStream_t st) {
 }
 template <typename DT, int TG, bool VEC, bool EK, bool FROM_H>
 hipError_t go_shrink(const GemmArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H>), dim3(a.s.max_tiles, a.split),
-                     dim3(kShrinkWaves * kWave), 0, st, a);
+  if (a.shrink_waves == 4)
+    hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H, 4>), dim3(a.s.max_tiles, a.split),
+                       dim3(4 * kWave), 0, st, a);
+  else if (a.shrink_waves == 8)
+    hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H, 8>), dim3(a.s.max_tiles, a.split),
+                       dim3(8 * kWave), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H, kShrinkWaves>),
+                       dim3(a.s.max_tiles, a.split), dim3(kShrinkWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
 

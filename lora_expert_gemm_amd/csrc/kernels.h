@@ -60,6 +60,7 @@ struct GemmArgs {
                            // or [R][r] per routed row (row mode)
   float *z_out;            // [split][cap][r] shrink partial sums written
   int split;               // workgroups sharing one shrink tile's contraction
+  int shrink_waves;        // waves per shrink workgroup (4, 8 or kShrinkWaves)
   RowShrinkArgs rs;        // row mode: the down shrink riding along with down
   int row_wgs;             // row mode: leading workgroups that run rs
   int waves;               // waves per workgroup of the GEMM kernels (16 columns each)
@@ -85,7 +86,8 @@ struct GemmArgs {
 constexpr int kRingSlots = 3;
 inline bool ring_slots_supported(int s) { return s == 0 || s == 3 || s == 4; }
 
-// Shrink kernels: one workgroup of kShrinkWaves waves per LoRA tile.
+// Shrink kernels: one workgroup per LoRA tile, of kShrinkWaves waves (or 4
+// or 8 when there are many tiles).
 constexpr int kShrinkWaves = 16;
 
 // Launchers (return hipGetLastError()).
