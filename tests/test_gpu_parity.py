@@ -300,6 +300,33 @@ def test_down_contraction_splits(T, H, I, E, k, NA, r, monkeypatch):
     check_close(outs["4"], outs["1"], "bf16", "ksplit 4 vs 1")
 
 
+# Shrink workgroups of 4, 8 and 16 waves (tile-mode LoRA): one tile's
+# contraction is cut into 16 / (row groups x token groups) parts per
+# workgroup, which meet in LDS; few waves leave one part per pair.
+SHRINK_WAVES = [
+    (200, 128, 256, 16, 2, 3, 16),  # 32-row blocks, r = 16
+    (160, 128, 256, 8, 2, 3, 16),   # 64-row blocks, r = 16
+    (300, 256, 192, 32, 4, 5, 40),  # 64-row blocks, r = 40: three 16-row groups of A
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r", SHRINK_WAVES)
+def test_shrink_workgroup_sizes(T, H, I, E, k, NA, r, monkeypatch):
+    """4-, 8- and 16-wave shrink workgroups each meet the oracle's tolerance."""
+    w = synth.Workload("shrink_waves", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
+                       adapters="uniform_with_none", seed=T * 5 + r)
+    d = synth.make_inputs(w)
+    rid, rw = oracle.ref_route(d["logits"], k)
+    ref = oracle_out(w, d, rid, rw)
+    for nw in ("4", "8", "16"):
+        monkeypatch.setenv("MOELORA_SHRINK_WAVES", nw)
+        run = Run(w, d).forward()
+        info = run.plan.info(T)
+        say(f"[parity] shrink waves={nw} {w}: plan {info}")
+        assert "lora_mode=tile" in info and f"shrink_waves={nw}" in info
+        check_close(run.out_f32(), ref, "bf16", f"shrink waves {nw}")
+
+
 SAMPLES = {"tiny_fp32": 8, "decode_bf16": 16, "illustrative_bf16": 12,
            "prefill_bf16": 20, "many_expert_bf16": 48, "dense_bf16": 8}
 
