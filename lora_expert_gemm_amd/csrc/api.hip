@@ -34,6 +34,7 @@ struct moelora_plan_s {
   int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
   bool rotate = true;      // streaming GEMMs: staggered slab walks for 4 KB-multiple weight rows
   int shrink_waves = 0;    // waves per shrink workgroup (0: by tile count)
+  bool tok_share = true;   // streaming GEMMs: tokens shared by a 4-wave workgroup in LDS
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -112,7 +113,7 @@ int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
 // split order.  At a third of the slots (the illustrative decode step) the
 // split measured 0-9 % slower, hence the quarter.
 constexpr int kComputeUnits = 256;  // MI355X
-int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d) {
+int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d, bool share) {
   if (tg == kTgTiled || d.dtype != MOELORA_BF16 || d.inter % 64 != 0) return 1;
   // tuning sweeps only: force the split count (1..8; every split keeps a slab)
   if (const char *v = getenv("MOELORA_KSPLIT_D")) {
@@ -120,7 +121,9 @@ int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d) {
     if (k >= 1 && k <= 8) return std::max(1, std::min(k, d.inter / 64));
   }
   const int nw = choose_down_rows(tg) == 32 ? 2 : 1;  // 16-row weight tiles per wave
-  const long long slots = (long long)kComputeUnits * std::max(1, 160 * 1024 / (kRingSlots * nw * 2048 * waves_d));
+  const int lds = share && waves_d == kShareWaves ? shared_lds_bytes(tg, nw, kRingSlots)
+                                                  : kRingSlots * nw * 2048 * waves_d;
+  const long long slots = (long long)kComputeUnits * std::max(1, 160 * 1024 / lds);
   const int cols = 16 * nw * waves_d;
   const long long grid = (long long)((s.H + cols - 1) / cols) *
                          std::max<long long>(std::min(s.E, s.R), (s.R + s.BM - 1) / s.BM);
@@ -153,7 +156,11 @@ struct Layout {
       off_zd, off_h, off_y, total;
 };
 
-Layout make_layout(const moelora_desc &d, int T) {
+// The weight stream of a projection runs through the LDS ring (bf16, the
+// contraction a multiple of 64), where 4-wave workgroups can share tokens.
+bool ring_ok(const moelora_desc &d, int K) { return d.dtype == MOELORA_BF16 && K % 64 == 0; }
+
+Layout make_layout(const moelora_desc &d, int T, bool share) {
   Layout L{};
   Shape &s = L.s;
   s.T = T;
@@ -175,12 +182,22 @@ Layout make_layout(const moelora_desc &d, int T) {
   const long long ne_used = std::max<long long>(1, std::min<long long>(d.n_experts, s.R));
   L.waves_gu = choose_waves(tg, true, d.inter, ne_used);
   L.waves_d = choose_waves(tg, false, d.inter, ne_used);
-  L.ksplit = choose_ksplit(d, s, tg, L.waves_d);
+  // Tokens shared by the waves of a workgroup make 4-wave workgroups pay
+  // for 32-row blocks too: gate_up always (many-expert 183 -> 176 us, dense
+  // 92 -> 82 us), down while its grid still holds 1024 such workgroups
+  // (many-expert 121 -> 108 us; the illustrative step's 384 went 154 -> 170
+  // us).
+  if (tg == kTgMid && share && ring_ok(d, d.hidden)) L.waves_gu = kShareWaves;
+  if (tg == kTgMid && share && ring_ok(d, d.inter) &&
+      (long long)((s.H + 127) / 128) * s.nblk >= 4 * kComputeUnits)
+    L.waves_d = kShareWaves;
+  const bool share_d = share && ring_ok(d, d.inter);
+  L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d);
   if (L.ksplit > 1 && L.waves_d != 4) {
     // split down GEMMs run with four-wave workgroups (the dense 64-token
     // step: 71 -> 56 us with 8 splits)
     L.waves_d = 4;
-    L.ksplit = choose_ksplit(d, s, tg, L.waves_d);
+    L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d);
   }
   L.split = choose_split(tg, s.R);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
@@ -300,10 +317,11 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   moelora_plan_s *p = new (std::nothrow) moelora_plan_s();
   if (!p) return MOELORA_ERR_INVALID_ARG;
   p->d = *desc;
+  if (const char *v = getenv("MOELORA_TOKSHARE")) p->tok_share = atoi(v) != 0;
   // the largest layout over every token count up to max_tokens: buckets
   // are contiguous ranges of T and sizes grow with T inside a bucket, so the
   // last T of each bucket bounds it
-  size_t ws = make_layout(p->d, p->d.max_tokens).total;
+  size_t ws = make_layout(p->d, p->d.max_tokens, p->tok_share).total;
   for (int T = p->d.max_tokens; T > 0;) {
     const int tg = choose_tg(p->d, T);
     int lo = 0, hi = T;  // smallest T' with the same bucket as T
@@ -311,7 +329,7 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
       const int mid = lo + (hi - lo) / 2;
       if (choose_tg(p->d, mid) == tg) hi = mid; else lo = mid + 1;
     }
-    ws = std::max(ws, make_layout(p->d, T).total);
+    ws = std::max(ws, make_layout(p->d, T, p->tok_share).total);
     T = lo - 1;
   }
   p->ws_bytes = ws;
@@ -338,7 +356,7 @@ moelora_status moelora_workspace_layout(moelora_plan_t plan, int32_t n_tokens,
                                         moelora_layout *out) {
   if (!plan || !out || n_tokens < 0 || n_tokens > plan->d.max_tokens)
     return MOELORA_ERR_INVALID_ARG;
-  const Layout L = make_layout(plan->d, n_tokens);
+  const Layout L = make_layout(plan->d, n_tokens, plan->tok_share);
   memset(out, 0, sizeof *out);
   out->block_m = L.s.BM;
   out->cap = L.s.cap;
@@ -358,12 +376,20 @@ moelora_status moelora_workspace_layout(moelora_plan_t plan, int32_t n_tokens,
   return MOELORA_OK;
 }
 
+namespace {
+// Whether a streaming projection (contraction K, wv waves) runs with shared tokens.
+bool shares(const moelora_plan_s *plan, int tg, int wv, int K) {
+  return plan->tok_share && tg != kTgTiled && wv == kShareWaves && plan->slots == kRingSlots &&
+         ring_ok(plan->d, K);
+}
+}  // namespace
+
 moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *buf,
                                  size_t buf_len) {
   if (!plan || !buf || buf_len == 0 || n_tokens < 0 || n_tokens > plan->d.max_tokens)
     return MOELORA_ERR_INVALID_ARG;
   const moelora_desc &d = plan->d;
-  const Layout L = make_layout(d, n_tokens);
+  const Layout L = make_layout(d, n_tokens, plan->tok_share);
   const int tg = L.s.BM / 16;
   const GemmVariant vg = variant(d, tg, d.hidden, true), vd = variant(d, tg, d.inter, true);
   const int wgu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
@@ -376,12 +402,12 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   snprintf(buf, buf_len,
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
            "k_tail_d=%d waves_gu=%d waves_d=%d down_rows=%d down_ksplit=%d lora_mode=%s "
-           "shrink_split=%d shrink_waves=%d cap=%d workspace=%zu",
+           "shrink_split=%d shrink_waves=%d tok_share_gu=%d tok_share_d=%d cap=%d workspace=%zu",
            vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
            k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, tg == kTgTiled ? 0 : down_rows,
            ksplit, d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile",
            L.split, plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(L.s, L.split),
-           L.s.cap, L.total);
+           (int)shares(plan, tg, wgu, d.hidden), (int)shares(plan, tg, wd, d.inter), L.s.cap, L.total);
   return MOELORA_OK;
 }
 
@@ -409,7 +435,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     if (p && !aligned(p, 16)) return MOELORA_ERR_INVALID_ARG;
   if (!aligned(workspace, kAlign)) return MOELORA_ERR_INVALID_ARG;
 
-  const Layout L = make_layout(d, n_tokens);
+  const Layout L = make_layout(d, n_tokens, plan->tok_share);
   if (workspace_bytes < L.total || L.total > plan->ws_bytes) return MOELORA_ERR_WORKSPACE;
   char *ws = static_cast<char *>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -479,6 +505,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   g.s = s;
   g.split = L.split;
   g.shrink_waves = plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(s, L.split);
+  g.tok_share = plan->tok_share;
   g.down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
   g.slots = plan->slots;
   // contraction splits of the down GEMM: only where its weight stream goes
@@ -556,7 +583,7 @@ moelora_status moelora_read_device_error(moelora_plan_t plan, const void *worksp
   if (!plan || !workspace || !error_bits) return MOELORA_ERR_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (hipStreamSynchronize(st) != hipSuccess) return MOELORA_ERR_HIP;
-  const Layout L = make_layout(plan->d, 0);
+  const Layout L = make_layout(plan->d, 0, plan->tok_share);
   if (hipMemcpy(error_bits, static_cast<const char *>(workspace) + L.off_error, 4,
                 hipMemcpyDeviceToHost) != hipSuccess)
     return MOELORA_ERR_HIP;

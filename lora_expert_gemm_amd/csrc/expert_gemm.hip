@@ -244,6 +244,113 @@ __device__ __forceinline__ void contract_dma_groups(const uint16_t *const *dsrc,
     contract_dma<1, NW, S>(dsrc, xr, K, kg, ri, rot, ring, acc0, acc1);
 }
 
+// Shared-token variant of contract_dma for workgroups of kShareWaves waves
+// that compute the same block against different weight rows: the block's
+// token rows go through one LDS ring of the workgroup instead of every
+// wave's registers, fetched with whole-line loads (global_load_lds_dwordx4
+// of 8 rows x 128 bytes, the chunk swizzle of the weight tiles) and each
+// fetched once for all the waves.  The 2 NG token loads of a slab are dealt
+// round the waves (kTI per wave; with more waves than loads a load is issued
+// twice, writing the same bytes).  Step j waits for the wave's own loads of
+// slab j, then at a workgroup barrier for everyone's (and for everyone to be
+// done with slab j - 1, whose slots it refills), so slabs j + 1 .. j + S - 1
+// are in flight while slab j is computed.  tok_row[row] is the token row of
+// block row row (0 <= row < 16 NG), tbase + tok_row * ld the start of its
+// contraction range.  Every wave of the workgroup must call this with the
+// same K, rot and NG (the barriers are counted).
+// One whole-line DMA: 64 lanes x 16 bytes from src (per lane) to lds (per
+// wave; lane l's bytes land at lds + 16 l).
+__device__ __forceinline__ void dma16(const uint16_t *src, unsigned char *lds, bool nontemporal) {
+  if (nontemporal)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0,
+                                     kCpolNonTemporal);
+  else
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+template <int NG, int NW, int S>
+__device__ __forceinline__ void contract_shared(const uint16_t *const *dsrc, const uint16_t *tbase,
+                                                size_t ld, const int *tok_row, int K, int kg,
+                                                int ri, int wave, int rot, unsigned char *tring,
+                                                int tslot, unsigned char *wring, f32x4_t *acc0,
+                                                f32x4_t *acc1) {
+  using M = Mma<uint16_t>;
+  constexpr int kTI = (2 * NG + kShareWaves - 1) / kShareWaves;  // token loads per wave
+  constexpr int kPer = 2 * NW + kTI;                              // loads per slab
+  constexpr int kYoung = (S - 2) * kPer;
+  static_assert(S >= 3 && kYoung < 64, "vmcnt immediate");
+  constexpr int kWait = 0x0f70 | (kYoung & 15) | ((kYoung >> 4) << 14);
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint16_t *tsrc[kTI];
+  int tq[kTI];
+#pragma unroll
+  for (int c = 0; c < kTI; ++c) {
+    const int q = (wave + c * kShareWaves) % (2 * NG);
+    const int row = 8 * q + (lane >> 3);
+    tq[c] = q;
+    tsrc[c] = tbase + (size_t)tok_row[row] * ld + 8 * ((lane & 7) ^ (lane >> 3));
+  }
+  const int nsl = K / 64;
+  auto slab = [&](int j) { return j + rot >= nsl ? j + rot - nsl : j + rot; };
+  auto issue = [&](int j, int p) {
+    j = slab(j);
+    unsigned char *d = wring + p * NW * 2048;
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(dsrc[2 * t + i] + 64 * j, d + t * 2048 + i * 1024, true);
+    unsigned char *td = tring + p * tslot;
+#pragma unroll
+    for (int c = 0; c < kTI; ++c) dma16(tsrc[c] + 64 * j, td + tq[c] * 1024, false);
+  };
+  auto compute = [&](int p) {
+    const unsigned char *d = wring + p * NW * 2048 + ri * 128;
+    const unsigned char *td = tring + p * tslot + ri * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = ((4 * h + kg) ^ (ri & 7)) << 4;
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(d + c);
+      const u32x4_t a1 = NW == 2 ? *reinterpret_cast<const u32x4_t *>(d + 2048 + c) : a0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(td + g * 2048 + c);
+        M::step(acc0[g], a0, b);
+        if (NW == 2) M::step(acc1[g], a1, b);
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) issue(min(j, nsl - 1), j);
+  for (int j = 0; j < nsl; ++j) {
+    __builtin_amdgcn_s_waitcnt(kWait);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(j + S - 1, nsl - 1), (j + S - 1) % S);
+    compute(j % S);
+  }
+  // vmcnt(0): no load of the rings may land after the wave leaves them
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
+// contract_shared over the block's ntg leading token groups.
+template <int TG, int NW, int S>
+__device__ __forceinline__ void contract_shared_groups(const uint16_t *const *dsrc,
+                                                       const uint16_t *tbase, size_t ld,
+                                                       const int *tok_row, int ntg, int K, int kg,
+                                                       int ri, int wave, int rot,
+                                                       unsigned char *tring, unsigned char *wring,
+                                                       f32x4_t *acc0, f32x4_t *acc1) {
+  constexpr int tslot = TG * 2048;
+  if (TG >= 4 && ntg > 2)
+    contract_shared<TG, NW, S>(dsrc, tbase, ld, tok_row, K, kg, ri, wave, rot, tring, tslot, wring,
+                               acc0, acc1);
+  else if (TG >= 2 && ntg > 1)
+    contract_shared<(TG >= 2 ? 2 : 1), NW, S>(dsrc, tbase, ld, tok_row, K, kg, ri, wave, rot, tring,
+                                              tslot, wring, acc0, acc1);
+  else
+    contract_shared<1, NW, S>(dsrc, tbase, ld, tok_row, K, kg, ri, wave, rot, tring, tslot, wring,
+                              acc0, acc1);
+}
 // Starting slab of a workgroup's weight walk (contract_dma): staggered over
 // workgroups when a.rotate is set, else 0.
 __device__ __forceinline__ int walk_start(const GemmArgs &a, int K) {
@@ -431,8 +538,9 @@ __device__ __forceinline__ GemmTile gemm_tile(int nblk, int bid, int nb) {
 // real rows (padding rows are skipped by every reader).
 // MODE: 0 no LoRA, 1 tile-wise (z per sorted position, split partials),
 // 2 row-wise (z per routed row).  S > 0: weights streamed through an S-slot
-// LDS ring per wave (contract_dma).
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, int S>
+// LDS ring per wave (contract_dma); SH: with the block's tokens shared by
+// the workgroup's kShareWaves waves (contract_shared).
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, int S, bool SH = false>
 __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
@@ -443,7 +551,9 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   const int e = a.al.block_expert[blk];  // -1 past the padded rows
   const int I = s.I, H = s.H;
   const int n0 = (gt.nt * a.waves + wave) * 16;
-  if (e < 0 || n0 >= I) return;
+  // (SH: a wave past the last column still takes part in the workgroup's
+  // token loads and barriers, on clamped rows, and returns after them)
+  if (e < 0 || (!SH && n0 >= I)) return;
   const int nrow = min(n0 + ri, I - 1);
   const DT *wg = static_cast<const DT *>(a.W) + ((size_t)e * 2 * I + nrow) * H;
   const DT *wu = wg + (size_t)I * H;
@@ -486,9 +596,24 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
       dsrc[i] = g;
       dsrc[2 + i] = g + (size_t)I * H;
     }
-    contract_dma_groups<TG, 2, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                  active_groups<TG>(a, blk), H, kg, ri, walk_start(a, H),
-                                  smem + wave * S * 4096, ag, au);
+    if constexpr (SH) {
+      int *tok_row = reinterpret_cast<int *>(smem);
+      if (threadIdx.x < BM) {
+        const int p = a.al.sorted_rows[blk * BM + threadIdx.x];
+        tok_row[threadIdx.x] = (p < s.R ? p : a.al.sorted_rows[blk * BM]) / s.k;
+      }
+      __syncthreads();
+      unsigned char *tring = smem + kTokRowBytes;
+      contract_shared_groups<TG, 2, S>(dsrc, static_cast<const uint16_t *>(a.x), (size_t)H, tok_row,
+                                       active_groups<TG>(a, blk), H, kg, ri, wave,
+                                       walk_start(a, H), tring,
+                                       tring + S * TG * 2048 + wave * S * 4096, ag, au);
+      if (n0 >= I) return;
+    } else {
+      contract_dma_groups<TG, 2, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
+                                    active_groups<TG>(a, blk), H, kg, ri, walk_start(a, H),
+                                    smem + wave * S * 4096, ag, au);
+    }
   } else {
     contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, active_groups<TG>(a, blk), H, kg, ag, au);
   }
@@ -525,7 +650,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
 // the combine.  With a.ksplit > 1 (LDS ring only) the contraction is split
 // over workgroups: split q sums its slab range into y[q] (the expand goes to
 // split 0), and the combine adds the partials in split order.
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2, int S>
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2, int S,
+          bool SH = false>
 __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
@@ -564,7 +690,7 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   // R2: the wave owns two 16-row tiles (rows m0 .. m0+31), two weight
   // streams against one set of h fragments
   const int m0 = (nt * a.waves + wave) * (R2 ? 32 : 16);
-  if (e < 0 || m0 >= H) return;
+  if (e < 0 || (!SH && m0 >= H)) return;  // (SH: as in k_gate_up)
   const int mrow = min(m0 + ri, H - 1);
   const int mrow1 = R2 ? min(m0 + 16 + ri, H - 1) : mrow;
   const DT *wd = static_cast<const DT *>(a.W) + ((size_t)e * H + mrow) * I;
@@ -603,9 +729,23 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
         dsrc[2 * t + i] = static_cast<const uint16_t *>(a.W) + ((size_t)e * H + min(m0 + r, H - 1)) * I +
                           k0 + 8 * ((lane & 7) ^ (r & 7));
       }
-    contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                   active_groups<TG>(a, blk), kn, kg, ri, walk_start(a, kn),
-                                   smem + wave * S * NW * 2048, acc, acc1);
+    if constexpr (SH) {
+      int *tok_row = reinterpret_cast<int *>(smem);
+      if (threadIdx.x < BM)
+        tok_row[threadIdx.x] =
+            blk * BM + (a.al.sorted_rows[blk * BM + threadIdx.x] < s.R ? (int)threadIdx.x : 0);
+      __syncthreads();
+      unsigned char *tring = smem + kTokRowBytes;
+      contract_shared_groups<TG, NW, S>(dsrc, static_cast<const uint16_t *>(a.h) + k0, (size_t)I,
+                                        tok_row, active_groups<TG>(a, blk), kn, kg, ri, wave,
+                                        walk_start(a, kn), tring,
+                                        tring + S * TG * 2048 + wave * S * NW * 2048, acc, acc1);
+      if (m0 >= H) return;
+    } else {
+      contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
+                                     active_groups<TG>(a, blk), kn, kg, ri, walk_start(a, kn),
+                                     smem + wave * S * NW * 2048, acc, acc1);
+    }
   } else {
     contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
   }
@@ -878,10 +1018,11 @@ template <int TG, bool GATE_UP> constexpr int unroll_for() {
   return TG == 1 && !GATE_UP ? 6 : TG <= 2 ? 4 : 2;
 }
 
-template <typename DT, int TG, bool VEC, bool EK, int MODE, int S>
+template <typename DT, int TG, bool VEC, bool EK, int MODE, int S, bool SH = false>
 hipError_t launch_gu(const GemmArgs &a, int ntn, hipStream_t st) {
-  auto kern = k_gate_up<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE, S>;
-  const int lds = S * 4096 * a.waves;  // two 16-row tiles (gate, up) per wave
+  auto kern = k_gate_up<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE, S, SH>;
+  // two 16-row tiles (gate, up) per wave, plus the shared token ring
+  const int lds = SH ? shared_lds_bytes(TG, 2, S) : S * 4096 * a.waves;
   if (S > 0) {
     const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -896,17 +1037,20 @@ hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
   const int ntn = (a.s.I + cols - 1) / cols;
   if constexpr (sizeof(DT) == 2 && VEC && EK) {
     if (a.s.H % 64 == 0) {
-      if (a.slots == 3) return launch_gu<DT, TG, VEC, EK, MODE, 3>(a, ntn, st);
+      if (a.slots == 3)
+        return a.tok_share && a.waves == kShareWaves
+                   ? launch_gu<DT, TG, VEC, EK, MODE, 3, true>(a, ntn, st)
+                   : launch_gu<DT, TG, VEC, EK, MODE, 3>(a, ntn, st);
       if (a.slots == 4) return launch_gu<DT, TG, VEC, EK, MODE, 4>(a, ntn, st);
     }
   }
   return launch_gu<DT, TG, VEC, EK, MODE, 0>(a, ntn, st);
 }
-template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2, int S>
+template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2, int S, bool SH = false>
 hipError_t launch_d(const GemmArgs &a, int ntn, hipStream_t st) {
-  auto kern = k_down<DT, TG, unroll_for<TG, R2>(), VEC, EK, MODE, R2, S>;
+  auto kern = k_down<DT, TG, unroll_for<TG, R2>(), VEC, EK, MODE, R2, S, SH>;
   const int extra = MODE == 2 ? a.row_wgs : 0;
-  const int lds = S * (R2 ? 4096 : 2048) * a.waves;
+  const int lds = SH ? shared_lds_bytes(TG, R2 ? 2 : 1, S) : S * (R2 ? 4096 : 2048) * a.waves;
   if (S > 0) {
     const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -920,7 +1064,10 @@ template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2>
 hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
   if constexpr (sizeof(DT) == 2 && VEC && EK) {
     if (a.s.I % 64 == 0) {
-      if (a.slots == 3) return launch_d<DT, TG, VEC, EK, MODE, R2, 3>(a, ntn, st);
+      if (a.slots == 3)
+        return a.tok_share && a.waves == kShareWaves
+                   ? launch_d<DT, TG, VEC, EK, MODE, R2, 3, true>(a, ntn, st)
+                   : launch_d<DT, TG, VEC, EK, MODE, R2, 3>(a, ntn, st);
       if (a.slots == 4) return launch_d<DT, TG, VEC, EK, MODE, R2, 4>(a, ntn, st);
     }
   }

@@ -69,6 +69,8 @@ struct GemmArgs {
                            // (bf16, contraction a multiple of 64); 0: loads into registers
   int ksplit;              // streaming down GEMM with the LDS ring: contraction splits, each
                            // writing its own partial y (1: none)
+  int tok_share;           // LDS ring, 4-wave workgroups, 3 slots: the block's tokens fetched
+                           // once per workgroup into a shared LDS ring (0: per wave)
   int rotate;              // LDS ring: workgroups start their contraction walk at staggered
                            // slabs (weight rows a multiple of 4 KB), 0: all at slab 0
   int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
@@ -85,6 +87,16 @@ struct GemmArgs {
 // (at least 3: a two-slot ring gave wrong outputs).
 constexpr int kRingSlots = 3;
 inline bool ring_slots_supported(int s) { return s == 0 || s == 3 || s == 4; }
+
+// Workgroups of kShareWaves waves with a 3-slot ring fetch the block's tokens
+// once into a shared LDS ring (GemmArgs::tok_share).  Their dynamic LDS:
+// token rows table, token ring, the waves' weight rings (NW 16-row tiles
+// each).
+constexpr int kShareWaves = 4;
+constexpr int kTokRowBytes = 256;
+constexpr int shared_lds_bytes(int TG, int NW, int S) {
+  return kTokRowBytes + S * TG * 2048 + kShareWaves * S * NW * 2048;
+}
 
 // Shrink kernels: one workgroup per LoRA tile, of kShrinkWaves waves (or 4
 // or 8 when there are many tiles).

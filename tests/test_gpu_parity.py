@@ -327,6 +327,47 @@ def test_shrink_workgroup_sizes(T, H, I, E, k, NA, r, monkeypatch):
         check_close(run.out_f32(), ref, "bf16", f"shrink waves {nw}")
 
 
+# Tokens shared by the four waves of a workgroup through an LDS ring, against
+# tokens loaded by each wave: same MFMAs in the same slab order on the same
+# token rows, so at equal waves (4) and one contraction split the outputs
+# are identical bit for bit.  16-, 32- and 64-row blocks, row-wise and
+# tile-wise LoRA, a dense layer, ragged last column tiles (gate_up: I = 200,
+# where the down contraction cannot use the ring; down: H = 320).
+TOKSHARE = [
+    (16, 256, 320, 8, 2, 3, 16),    # 16-row blocks, row-wise LoRA
+    (24, 256, 200, 4, 2, 3, 16),    # 32-row blocks, row-wise LoRA, ragged gate_up columns
+    (24, 320, 256, 4, 2, 3, 16),    # 32-row blocks, ragged down columns
+    (200, 128, 256, 16, 2, 3, 16),  # 32-row blocks, tile-wise LoRA
+    (160, 128, 256, 8, 2, 3, 16),   # 64-row blocks, tile-wise LoRA
+    (40, 128, 512, 1, 1, 3, 16),    # dense
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r", TOKSHARE)
+def test_shared_token_ring(T, H, I, E, k, NA, r, monkeypatch):
+    """Shared-token and per-wave-token streaming GEMMs agree bit for bit and
+    meet the oracle's tolerance."""
+    w = synth.Workload("tokshare", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
+                       adapters="uniform_with_none", seed=T * 3 + I)
+    d = synth.make_inputs(w)
+    rid, rw = oracle.ref_route(d["logits"], k)
+    ref = oracle_out(w, d, rid, rw)
+    monkeypatch.setenv("MOELORA_WAVES_GU", "4")
+    monkeypatch.setenv("MOELORA_WAVES_D", "4")
+    monkeypatch.setenv("MOELORA_KSPLIT_D", "1")
+    outs = {}
+    for sh in ("1", "0"):
+        monkeypatch.setenv("MOELORA_TOKSHARE", sh)
+        run = Run(w, d).forward()
+        info = run.plan.info(T)
+        say(f"[parity] tokshare={sh} {w}: plan {info}")
+        share_d = sh if I % 64 == 0 else "0"
+        assert f"tok_share_gu={sh}" in info and f"tok_share_d={share_d}" in info
+        outs[sh] = run.out.cpu().numpy().copy()
+        check_close(run.out_f32(), ref, "bf16", f"tokshare {sh}")
+    assert np.array_equal(outs["1"], outs["0"])
+
+
 SAMPLES = {"tiny_fp32": 8, "decode_bf16": 16, "illustrative_bf16": 12,
            "prefill_bf16": 20, "many_expert_bf16": 48, "dense_bf16": 8}
 
