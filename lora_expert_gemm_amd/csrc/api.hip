@@ -113,14 +113,15 @@ int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
 // split order.  At a third of the slots (the illustrative decode step) the
 // split measured 0-9 % slower, hence the quarter.
 constexpr int kComputeUnits = 256;  // MI355X
-int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d, bool share) {
+int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d, bool share,
+                  int down_rows) {
   if (tg == kTgTiled || d.dtype != MOELORA_BF16 || d.inter % 64 != 0) return 1;
   // tuning sweeps only: force the split count (1..8; every split keeps a slab)
   if (const char *v = getenv("MOELORA_KSPLIT_D")) {
     const int k = atoi(v);
     if (k >= 1 && k <= 8) return std::max(1, std::min(k, d.inter / 64));
   }
-  const int nw = choose_down_rows(tg) == 32 ? 2 : 1;  // 16-row weight tiles per wave
+  const int nw = down_rows == 32 ? 2 : 1;  // 16-row weight tiles per wave
   const int lds = share && waves_d == kShareWaves ? shared_lds_bytes(tg, nw, kRingSlots)
                                                   : kRingSlots * nw * 2048 * waves_d;
   const long long slots = (long long)kComputeUnits * std::max(1, 160 * 1024 / lds);
@@ -150,7 +151,7 @@ int choose_shrink_waves(const Shape &s, int split) {
 
 struct Layout {
   Shape s;
-  int waves_gu, waves_d, split, ksplit;
+  int waves_gu, waves_d, down_rows, split, ksplit;
   size_t off_error, off_counts, off_ids, off_w, off_sorted, off_bexp, off_seg, off_lseg,
       off_tiles, off_bts, off_bcnt, off_bbase, off_tperm, off_toff, off_rpos, off_zero, off_zgu,
       off_zd, off_h, off_y, total;
@@ -182,22 +183,25 @@ Layout make_layout(const moelora_desc &d, int T, bool share) {
   const long long ne_used = std::max<long long>(1, std::min<long long>(d.n_experts, s.R));
   L.waves_gu = choose_waves(tg, true, d.inter, ne_used);
   L.waves_d = choose_waves(tg, false, d.inter, ne_used);
+  L.down_rows = choose_down_rows(tg);
   // Tokens shared by the waves of a workgroup make 4-wave workgroups pay
   // for 32-row blocks too: gate_up always (many-expert 183 -> 176 us, dense
-  // 92 -> 82 us), down while its grid still holds 1024 such workgroups
-  // (many-expert 121 -> 108 us; the illustrative step's 384 went 154 -> 170
-  // us).
+  // 92 -> 82 us); down with 32-row tiles per wave while that grid holds 1024
+  // workgroups (many-expert 121 -> 108 us), else with 16-row tiles, which
+  // double the grid (the illustrative step's 384 workgroups: 154 us with two
+  // unshared waves, 170 us with 32-row tiles, 142 us with 16-row tiles).
   if (tg == kTgMid && share && ring_ok(d, d.hidden)) L.waves_gu = kShareWaves;
-  if (tg == kTgMid && share && ring_ok(d, d.inter) &&
-      (long long)((s.H + 127) / 128) * s.nblk >= 4 * kComputeUnits)
+  if (tg == kTgMid && share && ring_ok(d, d.inter)) {
     L.waves_d = kShareWaves;
+    if ((long long)((s.H + 127) / 128) * s.nblk < 4 * kComputeUnits) L.down_rows = 16;
+  }
   const bool share_d = share && ring_ok(d, d.inter);
-  L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d);
+  L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d, L.down_rows);
   if (L.ksplit > 1 && L.waves_d != 4) {
     // split down GEMMs run with four-wave workgroups (the dense 64-token
     // step: 71 -> 56 us with 8 splits)
     L.waves_d = 4;
-    L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d);
+    L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d, L.down_rows);
   }
   L.split = choose_split(tg, s.R);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
@@ -394,7 +398,7 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   const GemmVariant vg = variant(d, tg, d.hidden, true), vd = variant(d, tg, d.inter, true);
   const int wgu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
   const int wd = plan->waves_override_d ? plan->waves_override_d : L.waves_d;
-  const int down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
+  const int down_rows = plan->down_rows ? plan->down_rows : L.down_rows;
   const int ksplit = vd.bf16 && vd.vec && vd.even_k && d.inter % 64 == 0 && plan->slots != 0 &&
                              tg != kTgTiled
                          ? L.ksplit
@@ -506,7 +510,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   g.split = L.split;
   g.shrink_waves = plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(s, L.split);
   g.tok_share = plan->tok_share;
-  g.down_rows = plan->down_rows ? plan->down_rows : choose_down_rows(tg);
+  g.down_rows = plan->down_rows ? plan->down_rows : L.down_rows;
   g.slots = plan->slots;
   // contraction splits of the down GEMM: only where its weight stream goes
   // through the LDS ring
