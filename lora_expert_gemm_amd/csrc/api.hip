@@ -32,6 +32,7 @@ struct moelora_plan_s {
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
   int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
   int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
+  bool slots_forced = false;  // slots set by the caller's environment
   bool rotate = true;      // streaming GEMMs: staggered slab walks for 4 KB-multiple weight rows
   int shrink_waves = 0;    // waves per shrink workgroup (0: by tile count)
   bool tok_share = true;   // streaming GEMMs: tokens shared by a 4-wave workgroup in LDS
@@ -341,7 +342,10 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_DOWN_ROWS")) p->down_rows = atoi(v) == 32 ? 32 : atoi(v) == 16 ? 16 : 0;
-  if (const char *v = getenv("MOELORA_SLOTS")) p->slots = ring_slots_supported(atoi(v)) ? atoi(v) : 0;
+  if (const char *v = getenv("MOELORA_SLOTS")) {
+    p->slots = ring_slots_supported(atoi(v)) ? atoi(v) : 0;
+    p->slots_forced = true;
+  }
   if (const char *v = getenv("MOELORA_ROTATE")) p->rotate = atoi(v) != 0;
   if (const char *v = getenv("MOELORA_SHRINK_WAVES"))
     p->shrink_waves = atoi(v) == 4 || atoi(v) == 8 || atoi(v) == kShrinkWaves ? atoi(v) : 0;
@@ -383,7 +387,7 @@ moelora_status moelora_workspace_layout(moelora_plan_t plan, int32_t n_tokens,
 namespace {
 // Whether a streaming projection (contraction K, wv waves) runs with shared tokens.
 bool shares(const moelora_plan_s *plan, int tg, int wv, int K) {
-  return plan->tok_share && tg != kTgTiled && wv == kShareWaves && plan->slots == kRingSlots &&
+  return plan->tok_share && tg != kTgTiled && wv == kShareWaves && plan->slots != 0 &&
          ring_ok(plan->d, K);
 }
 }  // namespace
@@ -546,6 +550,10 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     a.z2 = z2_gu;
     a.waves = waves_gu;
     a.rotate = plan->rotate && (size_t)d.hidden * elem_bytes(d) % 4096 == 0;
+    // 16-row blocks' gate_up with shared tokens: a 4-slot ring (the decode
+    // step: 143 -> 139 us; 32-row blocks lose a workgroup per CU to it and
+    // slow down 6-20 %)
+    if (tg == kTgSmall && !plan->slots_forced && shares(plan, tg, waves_gu, d.hidden)) a.slots = 4;
     MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, true, vg, st) : launch_gate_up(a, vg, st));
   }
   MOELORA_TRY(mark());

@@ -1041,7 +1041,10 @@ hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
         return a.tok_share && a.waves == kShareWaves
                    ? launch_gu<DT, TG, VEC, EK, MODE, 3, true>(a, ntn, st)
                    : launch_gu<DT, TG, VEC, EK, MODE, 3>(a, ntn, st);
-      if (a.slots == 4) return launch_gu<DT, TG, VEC, EK, MODE, 4>(a, ntn, st);
+      if (a.slots == 4)
+        return a.tok_share && a.waves == kShareWaves
+                   ? launch_gu<DT, TG, VEC, EK, MODE, 4, true>(a, ntn, st)
+                   : launch_gu<DT, TG, VEC, EK, MODE, 4>(a, ntn, st);
     }
   }
   return launch_gu<DT, TG, VEC, EK, MODE, 0>(a, ntn, st);
@@ -1068,7 +1071,10 @@ hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
         return a.tok_share && a.waves == kShareWaves
                    ? launch_d<DT, TG, VEC, EK, MODE, R2, 3, true>(a, ntn, st)
                    : launch_d<DT, TG, VEC, EK, MODE, R2, 3>(a, ntn, st);
-      if (a.slots == 4) return launch_d<DT, TG, VEC, EK, MODE, R2, 4>(a, ntn, st);
+      if (a.slots == 4)
+        return a.tok_share && a.waves == kShareWaves
+                   ? launch_d<DT, TG, VEC, EK, MODE, R2, 4, true>(a, ntn, st)
+                   : launch_d<DT, TG, VEC, EK, MODE, R2, 4>(a, ntn, st);
     }
   }
   return launch_d<DT, TG, VEC, EK, MODE, R2, 0>(a, ntn, st);
