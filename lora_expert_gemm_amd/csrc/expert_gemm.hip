@@ -352,9 +352,11 @@ __device__ __forceinline__ void contract_shared_groups(const uint16_t *const *ds
                               acc0, acc1);
 }
 // Starting slab of a workgroup's weight walk (contract_dma): staggered over
-// workgroups when a.rotate is set, else 0.
-__device__ __forceinline__ int walk_start(const GemmArgs &a, int K) {
-  return a.rotate ? (int)((blockIdx.x * 7u) % (unsigned)(K / 64)) : 0;
+// column tiles when a.rotate is set, else 0.  Keyed on the column tile, not
+// the workgroup, so that the blocks of one expert, which stream the same
+// weight rows, walk them in step and can meet in L2.
+__device__ __forceinline__ int walk_start(const GemmArgs &a, int K, int col_tile) {
+  return a.rotate ? (int)(((unsigned)col_tile * 7u) % (unsigned)(K / 64)) : 0;
 }
 
 // z values of a lane's rows for the batched expand below: row mode, z of
@@ -606,12 +608,12 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
       unsigned char *tring = smem + kTokRowBytes;
       contract_shared_groups<TG, 2, S>(dsrc, static_cast<const uint16_t *>(a.x), (size_t)H, tok_row,
                                        active_groups<TG>(a, blk), H, kg, ri, wave,
-                                       walk_start(a, H), tring,
+                                       walk_start(a, H, gt.nt), tring,
                                        tring + S * TG * 2048 + wave * S * 4096, ag, au);
       if (n0 >= I) return;
     } else {
       contract_dma_groups<TG, 2, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                    active_groups<TG>(a, blk), H, kg, ri, walk_start(a, H),
+                                    active_groups<TG>(a, blk), H, kg, ri, walk_start(a, H, gt.nt),
                                     smem + wave * S * 4096, ag, au);
     }
   } else {
@@ -738,12 +740,12 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
       unsigned char *tring = smem + kTokRowBytes;
       contract_shared_groups<TG, NW, S>(dsrc, static_cast<const uint16_t *>(a.h) + k0, (size_t)I,
                                         tok_row, active_groups<TG>(a, blk), kn, kg, ri, wave,
-                                        walk_start(a, kn), tring,
+                                        walk_start(a, kn, gt.nt), tring,
                                         tring + S * TG * 2048 + wave * S * NW * 2048, acc, acc1);
       if (m0 >= H) return;
     } else {
       contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                     active_groups<TG>(a, blk), kn, kg, ri, walk_start(a, kn),
+                                     active_groups<TG>(a, blk), kn, kg, ri, walk_start(a, kn, gt.nt),
                                      smem + wave * S * NW * 2048, acc, acc1);
     }
   } else {
