@@ -57,8 +57,8 @@ def stage_of(kernel):
     k = short_name(kernel)
     for prefix, stage in _STAGES:
         if k.startswith(prefix):
-            if stage is None:  # k_shrink<DT, TG, VEC, EVEN_K, FROM_H>
-                return "shrink_down" if k.rstrip(">").split(",")[-1].strip() == "true" \
+            if stage is None:  # k_shrink<DT, TG, VEC, EVEN_K, FROM_H, waves>
+                return "shrink_down" if k.rstrip(">").split(",")[4].strip() == "true" \
                     else "shrink_gate_up"
             return stage
     return None

@@ -115,3 +115,19 @@ def test_roofline_bound_follows_the_ridge_point():
     rows = w.T * w.k
     flop, byts = 2.0 * rows * 2 * w.I * w.H, 2.0 * w.E * 2 * w.I * w.H + 2.0 * w.T * w.H
     assert not bench.hbm_bound({"p_flop": flop, "p_bytes": byts}, "p", "bf16")
+
+
+def test_profile_stage_names():
+    from lora_expert_gemm_amd import profiling as P
+    ns = "void moelora::(anonymous namespace)::"
+    cases = {
+        "k_shrink<unsigned short, 2, true, true, false, 8>(moelora::GemmArgs)": "shrink_gate_up",
+        "k_shrink<unsigned short, 2, true, true, true, 8>(moelora::GemmArgs)": "shrink_down",
+        "k_shrink<float, 1, true, false, true, 16>(moelora::GemmArgs)": "shrink_down",
+        "k_tiled_shrink<false, 64, true>(moelora::GemmArgs)": "shrink_gate_up",
+        "k_gate_up<unsigned short, 1, 4, true, true, 2, 4, true>(moelora::GemmArgs)": "gate_up",
+        "k_down<unsigned short, 2, 4, true, true, 1, true, 3, true>(moelora::GemmArgs)": "down",
+    }
+    for name, stage in cases.items():
+        assert P.stage_of(ns + name) == stage, name
+    assert P.stage_of("__amd_rocclr_copyBuffer") is None
