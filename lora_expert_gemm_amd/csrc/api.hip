@@ -87,7 +87,9 @@ int choose_tg(const moelora_desc &d, int T) {
 }
 
 // Waves per GEMM workgroup and weight rows per wave (measured with the
-// weight stream through the LDS ring).  16-row blocks: 4 waves for both
+// weight stream through the LDS ring and tokens loaded per wave; where the
+// tokens are shared through LDS, make_layout moves 32-row blocks to 4-wave
+// workgroups).  16-row blocks: 4 waves for both
 // projections (gate_up: 4 x (16 gate + 16 up) rows, ~2.5 % ahead of 2 waves;
 // down: 4 x 16 rows).  32-row blocks: down waves that own two 16-row tiles
 // each (2 waves x 32 rows; two weight streams share each h fragment, 6-17 %
