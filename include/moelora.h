@@ -83,7 +83,8 @@ typedef enum moelora_dtype { MOELORA_F32 = 0, MOELORA_BF16 = 1 } moelora_dtype;
 /* Shape of one layer.  Limits (else MOELORA_ERR_UNSUPPORTED):
  * 1 <= E <= 1024, E * (NA + 1) <= 8448, 1 <= k <= min(E, 32),
  * 0 <= NA, 0 <= r <= 256 (r >= 1 when NA >= 1), 1 <= H, I <= 65536,
- * 0 <= max_tokens, max_tokens * k <= 2^24; flags must be 0. */
+ * 0 <= max_tokens, max_tokens * k <= 2^24; flags: a combination of the
+ * MOELORA_FLAG_* bits below (any other bit: MOELORA_ERR_UNSUPPORTED). */
 typedef struct moelora_desc {
     int32_t max_tokens;
     int32_t hidden;      /* H */
@@ -93,17 +94,40 @@ typedef struct moelora_desc {
     int32_t n_adapters;  /* NA */
     int32_t rank;        /* r */
     int32_t dtype;       /* moelora_dtype */
-    uint32_t flags;      /* reserved, 0 */
+    uint32_t flags;      /* MOELORA_FLAG_* bits */
 } moelora_desc;
+
+/* Flags.  Both behaviours are always on in this library, so the bits are
+ * accepted and change nothing; they exist so a caller can state that it
+ * relies on them.
+ *   DETERMINISTIC    results are bitwise repeatable for a given plan, input
+ *                    and token count: split contractions (the split-K shrink
+ *                    of [AWS] "Kernel optimizations", the split down GEMM)
+ *                    write separate fp32 partials that their consumer adds
+ *                    in a fixed order; no kernel uses floating-point atomics.
+ *   DEBUG_CHECK_IDS  device-resident ids are range-checked: an expert id
+ *                    outside [0, E) drops its row, an adapter id outside
+ *                    [-1, NA) counts as -1, and either sets a bit of the
+ *                    device error word (moelora_read_device_error). */
+#define MOELORA_FLAG_DETERMINISTIC 1u
+#define MOELORA_FLAG_DEBUG_CHECK_IDS 2u
 
 typedef struct moelora_plan_s *moelora_plan_t;
 typedef struct ihipStream_t *moelora_stream_t; /* the same type as hipStream_t */
 
 /* Validate the shape and choose kernels, block size and split-K for every
  * token count up to max_tokens.  Host only: no device memory is touched and
- * no code is compiled or loaded.  *workspace_bytes receives the workspace a
- * forward of up to max_tokens tokens needs.  On success *plan must later be
- * released with moelora_plan_destroy. */
+ * no code is compiled or loaded; every kernel is compiled ahead of time and
+ * takes the token count as a run-time argument, and the choices are made
+ * here, once, for all token counts, because [AWS] "Execution optimizations"
+ * traces a tenfold time-to-first-token regression to kernels recompiled for
+ * each new context length.  Tuning switches in the environment (MOELORA_*)
+ * are read here and never by a forward.  *workspace_bytes receives the
+ * largest workspace any forward of 0..max_tokens tokens needs (every token
+ * count is checked).  On success *plan must later be released with
+ * moelora_plan_destroy.  Errors: MOELORA_ERR_INVALID_ARG for null
+ * pointers, MOELORA_ERR_UNSUPPORTED for a shape, dtype or flag outside the
+ * limits above. */
 MOELORA_API moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
                             size_t *workspace_bytes);
 

@@ -39,6 +39,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 DEVERR_EXPERT_ID, DEVERR_ADAPTER_ID = 1, 2
+FLAG_DETERMINISTIC, FLAG_DEBUG_CHECK_IDS = 1, 2
 N_STAGES = 6
 STAGES = ("route_align", "shrink_gate_up", "gate_up", "shrink_down", "down", "combine")
 
@@ -187,9 +188,9 @@ class Plan:
     _destroy_fn = _lib.moelora_plan_destroy  # ctypes function object (holds the library)
 
     def __init__(self, max_tokens, hidden, inter, n_experts, top_k, n_adapters, rank,
-                 dtype):
+                 dtype, flags=0):
         self.handle, self.workspace_bytes = moelora_plan(
-            max_tokens, hidden, inter, n_experts, top_k, n_adapters, rank, dtype)
+            max_tokens, hidden, inter, n_experts, top_k, n_adapters, rank, dtype, flags)
         self.desc = dict(max_tokens=max_tokens, hidden=hidden, inter=inter,
                          n_experts=n_experts, top_k=top_k, n_adapters=n_adapters,
                          rank=rank, dtype=dtype)

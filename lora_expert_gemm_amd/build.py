@@ -41,11 +41,25 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
+def _stale(src):
+    """Whether src's object is older than src or any header of csrc/ or include/."""
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [
+        os.path.join(d, f) for d in (CSRC, os.path.join(ROOT, "include"))
+        for f in os.listdir(d) if f.endswith(".h")]
+    return max(os.path.getmtime(p) for p in deps) > os.path.getmtime(obj)
+
+
+def build(verbose=False, incremental=False):
+    """Compile every source (incremental: only those whose object is stale) and link."""
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    todo = [s for s in SOURCES if not incremental or _stale(s)]
+    with ThreadPoolExecutor(max(1, len(todo))) as ex:
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,4 +72,4 @@ def build(verbose=False):
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)

@@ -26,16 +26,25 @@
 
 using namespace moelora;
 
+// Tuning switches, read from the environment once, by moelora_plan, and
+// fixed for the plan's lifetime (a forward never reads the environment).
+struct Tuning {
+  int tg = 0;              // streaming block size in 16-row groups, 1, 2 or 4 (0: by bucket)
+  int ksplit_d = 0;        // contraction splits of the streaming down GEMM, 1..8 (0: by grid)
+  bool tok_share = true;   // streaming GEMMs: tokens shared by a 4-wave workgroup in LDS
+  bool verbose = false;    // a failed launch prints its name and HIP error to stderr
+};
+
 struct moelora_plan_s {
   moelora_desc d;
   size_t ws_bytes;
+  Tuning tune;
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
   int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
   int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
   bool slots_forced = false;  // slots set by the caller's environment
   bool rotate = true;      // streaming GEMMs: staggered slab walks for 4 KB-multiple weight rows
   int shrink_waves = 0;    // waves per shrink workgroup (0: by tile count)
-  bool tok_share = true;   // streaming GEMMs: tokens shared by a 4-wave workgroup in LDS
   // stage timing
   bool timing = false;
   int max_calls = 0, n_calls = 0;
@@ -63,17 +72,14 @@ bool tiled_shrink_ok(const moelora_desc &d) { return d.rank <= 64; }
 bool fused_lora_ok(const moelora_desc &d, int K) {
   return tiled_shrink_ok(d) && d.rank % 32 == 0 && K % 64 == 0;
 }
-int choose_tg(const moelora_desc &d, int T) {
+int choose_tg(const moelora_desc &d, const Tuning &tu, int T) {
   const long long rows = (long long)T * d.top_k;
   const long long ne = std::max<long long>(1, std::min<long long>(d.n_experts, rows));
   // Streaming blocks: 16 rows while experts average at most 4 rows, then 32
   // rows (most experts' rows in one block, so their weights stream once,
   // without the register cost of 64-row blocks).
-  // tuning sweeps only: force the streaming block size (1, 2 or 4 groups of 16)
-  if (const char *v = getenv("MOELORA_TG")) {
-    const int tg = atoi(v);
-    if (tg == 1 || tg == 2 || tg == 4) return tg;
-  }
+  // tuning sweeps only: a forced streaming block size (1, 2 or 4 groups of 16)
+  if (tu.tg) return tu.tg;
   // One expert (a dense layer) at decode size: the grid is one or two blocks
   // wide, so the 128-row tiled kernel (43 workgroups for a 64-token step of
   // the 4096 x 11008 MLP: 698 us) and 64-row blocks (274 us) leave most CUs
@@ -116,14 +122,11 @@ int choose_down_rows(int tg) { return tg == kTgMid ? 32 : 16; }
 // split order.  At a third of the slots (the illustrative decode step) the
 // split measured 0-9 % slower, hence the quarter.
 constexpr int kComputeUnits = 256;  // MI355X
-int choose_ksplit(const moelora_desc &d, const Shape &s, int tg, int waves_d, bool share,
-                  int down_rows) {
+int choose_ksplit(const moelora_desc &d, const Tuning &tu, const Shape &s, int tg, int waves_d,
+                  bool share, int down_rows) {
   if (tg == kTgTiled || d.dtype != MOELORA_BF16 || d.inter % 64 != 0) return 1;
-  // tuning sweeps only: force the split count (1..8; every split keeps a slab)
-  if (const char *v = getenv("MOELORA_KSPLIT_D")) {
-    const int k = atoi(v);
-    if (k >= 1 && k <= 8) return std::max(1, std::min(k, d.inter / 64));
-  }
+  // tuning sweeps only: a forced split count (1..8; every split keeps a slab)
+  if (tu.ksplit_d) return std::max(1, std::min(tu.ksplit_d, d.inter / 64));
   const int nw = down_rows == 32 ? 2 : 1;  // 16-row weight tiles per wave
   const int lds = share && waves_d == kShareWaves ? shared_lds_bytes(tg, nw, kRingSlots)
                                                   : kRingSlots * nw * 2048 * waves_d;
@@ -164,7 +167,8 @@ struct Layout {
 // contraction a multiple of 64), where 4-wave workgroups can share tokens.
 bool ring_ok(const moelora_desc &d, int K) { return d.dtype == MOELORA_BF16 && K % 64 == 0; }
 
-Layout make_layout(const moelora_desc &d, int T, bool share) {
+Layout make_layout(const moelora_desc &d, const Tuning &tu, int T) {
+  const bool share = tu.tok_share;
   Layout L{};
   Shape &s = L.s;
   s.T = T;
@@ -175,7 +179,7 @@ Layout make_layout(const moelora_desc &d, int T, bool share) {
   s.NA = d.n_adapters;
   s.r = d.rank;
   s.R = T * d.top_k;
-  s.BM = 16 * choose_tg(d, T);
+  s.BM = 16 * choose_tg(d, tu, T);
   const long long ne = std::min<long long>(s.E, s.R);
   const long long bound = (long long)s.R + ne * (s.BM - 1);
   s.cap = (int)((bound + s.BM - 1) / s.BM * s.BM);
@@ -199,12 +203,12 @@ Layout make_layout(const moelora_desc &d, int T, bool share) {
     if ((long long)((s.H + 127) / 128) * s.nblk < 4 * kComputeUnits) L.down_rows = 16;
   }
   const bool share_d = share && ring_ok(d, d.inter);
-  L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d, L.down_rows);
+  L.ksplit = choose_ksplit(d, tu, s, tg, L.waves_d, share_d, L.down_rows);
   if (L.ksplit > 1 && L.waves_d != 4) {
     // split down GEMMs run with four-wave workgroups (the dense 64-token
     // step: 71 -> 56 us with 8 splits)
     L.waves_d = 4;
-    L.ksplit = choose_ksplit(d, s, tg, L.waves_d, share_d, L.down_rows);
+    L.ksplit = choose_ksplit(d, tu, s, tg, L.waves_d, share_d, L.down_rows);
   }
   L.split = choose_split(tg, s.R);
   const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
@@ -246,7 +250,8 @@ size_t elem_bytes(const moelora_desc &d) { return d.dtype == MOELORA_BF16 ? 2 : 
 
 moelora_status check_desc(const moelora_desc *d) {
   if (!d) return MOELORA_ERR_INVALID_ARG;
-  if (d->flags != 0) return MOELORA_ERR_UNSUPPORTED;
+  if (d->flags & ~(uint32_t)(MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_DEBUG_CHECK_IDS))
+    return MOELORA_ERR_UNSUPPORTED;
   if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
   if (d->n_experts < 1 || d->n_experts > 1024) return MOELORA_ERR_UNSUPPORTED;
   if (d->n_adapters < 0 || d->n_adapters > 255) return MOELORA_ERR_UNSUPPORTED;
@@ -291,9 +296,10 @@ int k_tail(const moelora_desc &d, int K) {
 }
 
 // A failed launch: MOELORA_ERR_HIP, and with MOELORA_VERBOSE set in the
-// environment a line on stderr naming the launch and the HIP error.
-moelora_status hip_failure(hipError_t err, const char *what, int line) {
-  if (getenv("MOELORA_VERBOSE"))
+// environment when the plan was made, a line on stderr naming the launch and
+// the HIP error.
+moelora_status hip_failure(bool verbose, hipError_t err, const char *what, int line) {
+  if (verbose)
     fprintf(stderr, "moelora_forward: %s (api.hip:%d) failed: %s (%d)\n", what, line,
             hipGetErrorString(err), (int)err);
   return MOELORA_ERR_HIP;
@@ -324,21 +330,23 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   moelora_plan_s *p = new (std::nothrow) moelora_plan_s();
   if (!p) return MOELORA_ERR_INVALID_ARG;
   p->d = *desc;
-  if (const char *v = getenv("MOELORA_TOKSHARE")) p->tok_share = atoi(v) != 0;
-  // the largest layout over every token count up to max_tokens: buckets
-  // are contiguous ranges of T and sizes grow with T inside a bucket, so the
-  // last T of each bucket bounds it
-  size_t ws = make_layout(p->d, p->d.max_tokens, p->tok_share).total;
-  for (int T = p->d.max_tokens; T > 0;) {
-    const int tg = choose_tg(p->d, T);
-    int lo = 0, hi = T;  // smallest T' with the same bucket as T
-    while (lo < hi) {
-      const int mid = lo + (hi - lo) / 2;
-      if (choose_tg(p->d, mid) == tg) hi = mid; else lo = mid + 1;
-    }
-    ws = std::max(ws, make_layout(p->d, T, p->tok_share).total);
-    T = lo - 1;
+  // tuning sweeps only (none is needed; the defaults are the measured choices)
+  if (const char *v = getenv("MOELORA_TOKSHARE")) p->tune.tok_share = atoi(v) != 0;
+  p->tune.verbose = getenv("MOELORA_VERBOSE") != nullptr;
+  if (const char *v = getenv("MOELORA_TG")) {
+    const int tg = atoi(v);
+    if (tg == 1 || tg == 2 || tg == 4) p->tune.tg = tg;
   }
+  if (const char *v = getenv("MOELORA_KSPLIT_D")) {
+    const int k = atoi(v);
+    if (k >= 1 && k <= 8) p->tune.ksplit_d = k;
+  }
+  // The largest layout over every token count up to max_tokens.  Sizes are
+  // not monotone in T (the shrink and down-GEMM split counts fall as T
+  // grows, and the block size changes between buckets), so every T is
+  // visited: make_layout is a few dozen integer operations.
+  size_t ws = make_layout(p->d, p->tune, 0).total;
+  for (int T = 1; T <= p->d.max_tokens; ++T) ws = std::max(ws, make_layout(p->d, p->tune, T).total);
   p->ws_bytes = ws;
   // tuning sweeps only: force the waves per GEMM workgroup (1..4)
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
@@ -366,7 +374,7 @@ moelora_status moelora_workspace_layout(moelora_plan_t plan, int32_t n_tokens,
                                         moelora_layout *out) {
   if (!plan || !out || n_tokens < 0 || n_tokens > plan->d.max_tokens)
     return MOELORA_ERR_INVALID_ARG;
-  const Layout L = make_layout(plan->d, n_tokens, plan->tok_share);
+  const Layout L = make_layout(plan->d, plan->tune, n_tokens);
   memset(out, 0, sizeof *out);
   out->block_m = L.s.BM;
   out->cap = L.s.cap;
@@ -389,7 +397,7 @@ moelora_status moelora_workspace_layout(moelora_plan_t plan, int32_t n_tokens,
 namespace {
 // Whether a streaming projection (contraction K, wv waves) runs with shared tokens.
 bool shares(const moelora_plan_s *plan, int tg, int wv, int K) {
-  return plan->tok_share && tg != kTgTiled && wv == kShareWaves && plan->slots != 0 &&
+  return plan->tune.tok_share && tg != kTgTiled && wv == kShareWaves && plan->slots != 0 &&
          ring_ok(plan->d, K);
 }
 }  // namespace
@@ -399,7 +407,7 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   if (!plan || !buf || buf_len == 0 || n_tokens < 0 || n_tokens > plan->d.max_tokens)
     return MOELORA_ERR_INVALID_ARG;
   const moelora_desc &d = plan->d;
-  const Layout L = make_layout(d, n_tokens, plan->tok_share);
+  const Layout L = make_layout(d, plan->tune, n_tokens);
   const int tg = L.s.BM / 16;
   const GemmVariant vg = variant(d, tg, d.hidden, true), vd = variant(d, tg, d.inter, true);
   const int wgu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
@@ -445,7 +453,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
     if (p && !aligned(p, 16)) return MOELORA_ERR_INVALID_ARG;
   if (!aligned(workspace, kAlign)) return MOELORA_ERR_INVALID_ARG;
 
-  const Layout L = make_layout(d, n_tokens, plan->tok_share);
+  const Layout L = make_layout(d, plan->tune, n_tokens);
   if (workspace_bytes < L.total || L.total > plan->ws_bytes) return MOELORA_ERR_WORKSPACE;
   char *ws = static_cast<char *>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -487,7 +495,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
 #define MOELORA_TRY(expr)                                                            \
   do {                                                                               \
     const hipError_t moelora_err_ = (expr);                                          \
-    if (moelora_err_ != hipSuccess) return hip_failure(moelora_err_, #expr, __LINE__); \
+    if (moelora_err_ != hipSuccess) return hip_failure(plan->tune.verbose, moelora_err_, #expr, __LINE__); \
   } while (0)
 
   const int waves_gu = plan->waves_override_gu ? plan->waves_override_gu : L.waves_gu;
@@ -515,7 +523,7 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   g.s = s;
   g.split = L.split;
   g.shrink_waves = plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(s, L.split);
-  g.tok_share = plan->tok_share;
+  g.tok_share = plan->tune.tok_share;
   g.down_rows = plan->down_rows ? plan->down_rows : L.down_rows;
   g.slots = plan->slots;
   // contraction splits of the down GEMM: only where its weight stream goes
@@ -599,7 +607,7 @@ moelora_status moelora_read_device_error(moelora_plan_t plan, const void *worksp
   if (!plan || !workspace || !error_bits) return MOELORA_ERR_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (hipStreamSynchronize(st) != hipSuccess) return MOELORA_ERR_HIP;
-  const Layout L = make_layout(plan->d, 0, plan->tok_share);
+  const Layout L = make_layout(plan->d, plan->tune, 0);
   if (hipMemcpy(error_bits, static_cast<const char *>(workspace) + L.off_error, 4,
                 hipMemcpyDeviceToHost) != hipSuccess)
     return MOELORA_ERR_HIP;

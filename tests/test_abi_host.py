@@ -44,12 +44,65 @@ DECODE = dict(max_tokens=16, hidden=2880, inter=2880, n_experts=32, top_k=4,
     (dict(dtype=7), lib.ERR_UNSUPPORTED),
     (dict(hidden=0), lib.ERR_UNSUPPORTED),
     (dict(max_tokens=-1), lib.ERR_UNSUPPORTED),
-    (dict(flags=1), lib.ERR_UNSUPPORTED),
+    (dict(flags=4), lib.ERR_UNSUPPORTED),                     # an undefined flag bit
+    (dict(flags=0x80000000), lib.ERR_UNSUPPORTED),
 ])
 def test_plan_rejects_out_of_range_shapes(bad, status):
     with pytest.raises(lib.MoeLoraError) as ei:
         lib.moelora_plan(**dict(DECODE, **bad))
     assert ei.value.status == status
+
+
+@pytest.mark.parametrize("flags", [
+    lib.FLAG_DETERMINISTIC, lib.FLAG_DEBUG_CHECK_IDS,
+    lib.FLAG_DETERMINISTIC | lib.FLAG_DEBUG_CHECK_IDS])
+def test_plan_accepts_the_defined_flags(flags):
+    """Both behaviours are always on, so the flags change neither the kernels
+    nor the workspace."""
+    p0 = lib.Plan(**DECODE)
+    p = lib.Plan(**DECODE, flags=flags)
+    assert p.workspace_bytes == p0.workspace_bytes
+    for T in (1, 7, 16):
+        assert p.info(T) == p0.info(T)
+
+
+def _info(p, T):
+    return dict(kv.split("=") for kv in p.info(T).split())
+
+
+# Shapes whose max_tokens sits inside a token-count bucket, where the
+# workspace of a smaller token count can exceed that of max_tokens (the
+# split counts of the shrink and of the down GEMM fall as T grows).
+SCAN = [
+    dict(max_tokens=100, hidden=4096, inter=11008, n_experts=1, top_k=1, n_adapters=16,
+         rank=32, dtype=lib.BF16),
+    dict(max_tokens=300, hidden=2048, inter=768, n_experts=128, top_k=8, n_adapters=32,
+         rank=16, dtype=lib.BF16),
+    dict(max_tokens=77, hidden=2880, inter=2880, n_experts=32, top_k=4, n_adapters=8,
+         rank=32, dtype=lib.BF16),
+    dict(max_tokens=50, hidden=128, inter=256, n_experts=4, top_k=2, n_adapters=2, rank=8,
+         dtype=lib.F32),
+]
+
+
+@pytest.mark.parametrize("desc", SCAN)
+def test_plan_workspace_covers_every_token_count(desc):
+    p = lib.Plan(**desc)
+    need = [int(_info(p, T)["workspace"]) for T in range(desc["max_tokens"] + 1)]
+    assert max(need) == p.workspace_bytes
+
+
+def test_tuning_switches_are_read_at_plan_time(monkeypatch):
+    """A forward never reads the environment: a switch set after the plan
+    changes nothing, and one set before it holds after it is unset."""
+    monkeypatch.delenv("MOELORA_TG", raising=False)
+    p = lib.Plan(**DECODE)
+    before = [p.info(T) for T in (1, 8, 16)]
+    monkeypatch.setenv("MOELORA_TG", "4")
+    assert [p.info(T) for T in (1, 8, 16)] == before
+    forced = lib.Plan(**DECODE)
+    monkeypatch.delenv("MOELORA_TG")
+    assert all(_info(forced, T)["block_m"] == "64" for T in (1, 8, 16))
 
 
 @pytest.mark.parametrize("desc", [
