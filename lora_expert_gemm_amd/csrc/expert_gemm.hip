@@ -143,33 +143,45 @@ __device__ __forceinline__ void contract(const DT *w0, const DT *w1, const DT *c
 // rows each (lane l: row l / 8, one 16-byte chunk), so every load
 // instruction covers whole 128-byte lines -- the register path above has a
 // lane per (row, chunk of a 64-byte half line) and streams slower.  Slabs go
-// round a per-wave ring of S slots in LDS: step j fetches slab j + S - 1 and
-// the tokens of slab j + 1, then waits for slab j and its tokens, which (the
-// counter retiring in issue order) also lands slab j + 1, so slab j + S - 1
-// is in flight while slab j is computed.  A two-slot ring gave wrong
-// outputs (80 % off; the cause was not isolated -- there the slab read at
-// step j is landed by step j's own wait, here by step j - 1's), so S >= 3.
+// round a per-wave ring of S >= 2 slots in LDS.  Step j first waits until
+// the LDS reads of step j - 1 have returned (they read the slot refilled
+// now), then issues the P = 2 NW + 2 NG loads of the step: slab j + S - 1
+// into its slot and the tokens of slab j + 1 into registers; then it waits
+// with vmcnt(P), i.e. for everything but the step's own P loads, and
+// computes slab j.  Every load of slab j was issued before this step's
+// loads (at step j - S + 1, or before the loop), and vector-memory loads,
+// direct-to-LDS ones included, retire in issue order, so the wait has
+// landed slab j in LDS and its tokens in registers (with S >= 3 it has also
+// landed slabs j + 1 .. j + S - 2).  Compiler barriers keep each step's
+// loads on their side of its waits, and each slab issues exactly P vector
+// loads (past the end the last slab is fetched again into a free slot), so
+// the fixed count holds; the kernels use no scratch memory, whose reloads
+// would be vector loads too.
 // The MFMA operand of lane l (row l % 16, chunk l / 16 of a 32-wide step) is then
 // one ds_read_b128.  Chunk c of tile row r sits at chunk c ^ (r % 8) of its
 // LDS row, so the 16 rows read at one chunk spread over distinct banks.
-// Tokens (L2-resident, shared by every workgroup of the block) are still
-// loaded straight into registers, one slab ahead.  Each slab issues the same
-// number of loads (past the end the last slab is fetched again into a free
-// slot), which makes a fixed vmcnt the wait for "slab j and its tokens".
+// Tokens (L2-resident, shared by every workgroup of the block) are loaded
+// straight into registers, one slab ahead.
 // Weight loads are marked non-temporal: each line is read once.  rot
 // (0 <= rot < K / 64) starts the walk at slab rot and wraps around: with
 // row strides that are multiples of 4 KB, workgroups that walk the same
 // slab columns at once stream ~13 % slower than staggered ones.
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; an all-ones field waits for nothing).
+constexpr int waitcnt_vm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xc07f;  // lgkmcnt(0): every LDS read has returned
 template <int NG, int NW, int S>
 __device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
                                              const uint16_t *const *xr, int K, int kg, int ri,
                                              int rot, unsigned char *ring, f32x4_t *acc0,
                                              f32x4_t *acc1) {
   using M = Mma<uint16_t>;
+  static_assert(S >= 2, "a slot is refilled while another is read");
   constexpr int kSlot = NW * 2048;
-  constexpr int kYoung = 2 * NW + 2 * NG;  // loads issued after a slab's token loads
-  static_assert(kYoung < 16, "vmcnt immediate");
-  constexpr int kWait = 0x0f70 | kYoung;   // vmcnt(kYoung), expcnt / lgkmcnt unconstrained
+  constexpr int kPer = 2 * NW + 2 * NG;    // vector loads issued per step
+  static_assert(kPer < 64, "vmcnt immediate");
+  constexpr int kWait = waitcnt_vm(kPer);  // all but the step's own loads
   const int nsl = K / 64;
   auto slab = [&](int j) { return j + rot >= nsl ? j + rot - nsl : j + rot; };
   auto dma = [&](int j, int p) {
@@ -212,8 +224,12 @@ __device__ __forceinline__ void contract_dma(const uint16_t *const *dsrc,
   // one slab: fetch slab j + S - 1 and the tokens of slab j + 1, then the
   // MFMAs of slab j once it and its tokens (tk) have arrived
   auto step = [&](int j, const Tok &tk, Tok &tn) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot (j + S - 1) % S has been read out
+    asm volatile("" ::: "memory");
     dma(min(j + S - 1, nsl - 1), (j + S - 1) % S);
     tload(tn, min(j + 1, nsl - 1));
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWait);
     asm volatile("" ::: "memory");
     compute(j % S, tk);
@@ -251,10 +267,13 @@ __device__ __forceinline__ void contract_dma_groups(const uint16_t *const *dsrc,
 // of 8 rows x 128 bytes, the chunk swizzle of the weight tiles) and each
 // fetched once for all the waves.  The 2 NG token loads of a slab are dealt
 // round the waves (kTI per wave; with more waves than loads a load is issued
-// twice, writing the same bytes).  Step j waits for the wave's own loads of
-// slab j, then at a workgroup barrier for everyone's (and for everyone to be
-// done with slab j - 1, whose slots it refills), so slabs j + 1 .. j + S - 1
-// are in flight while slab j is computed.  tok_row[row] is the token row of
+// twice, writing the same bytes).  Step j waits until the wave's own loads
+// of slab j have landed (vmcnt leaves only the loads of the S - 2 younger
+// slabs in flight) and its LDS reads of slab j - 1 have returned (lgkmcnt 0),
+// then meets the other waves at a workgroup barrier: after it, every wave's
+// share of slab j is in LDS and nobody reads slab j - 1 any more, so its
+// slots are refilled with slab j + S - 1, and slabs j + 1 .. j + S - 1 are
+// in flight while slab j is computed.  tok_row[row] is the token row of
 // block row row (0 <= row < 16 NG), tbase + tok_row * ld the start of its
 // contraction range.  Every wave of the workgroup must call this with the
 // same K, rot and NG (the barriers are counted).
@@ -276,9 +295,9 @@ __device__ __forceinline__ void contract_shared(const uint16_t *const *dsrc, con
   using M = Mma<uint16_t>;
   constexpr int kTI = (2 * NG + kShareWaves - 1) / kShareWaves;  // token loads per wave
   constexpr int kPer = 2 * NW + kTI;                              // loads per slab
-  constexpr int kYoung = (S - 2) * kPer;
-  static_assert(S >= 3 && kYoung < 64, "vmcnt immediate");
-  constexpr int kWait = 0x0f70 | (kYoung & 15) | ((kYoung >> 4) << 14);
+  constexpr int kYoung = (S - 2) * kPer;  // loads of the slabs issued after slab j
+  static_assert(S >= 2 && kYoung < 64, "vmcnt immediate");
+  constexpr int kWait = waitcnt_vm_lgkm0(kYoung);
   const int lane = threadIdx.x & (kWave - 1);
   const uint16_t *tsrc[kTI];
   int tq[kTI];
@@ -321,6 +340,7 @@ __device__ __forceinline__ void contract_shared(const uint16_t *const *dsrc, con
 #pragma unroll
   for (int j = 0; j < S - 1; ++j) issue(min(j, nsl - 1), j);
   for (int j = 0; j < nsl; ++j) {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWait);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -1039,6 +1059,10 @@ hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
   const int ntn = (a.s.I + cols - 1) / cols;
   if constexpr (sizeof(DT) == 2 && VEC && EK) {
     if (a.s.H % 64 == 0) {
+      if (a.slots == 2)
+        return a.tok_share && a.waves == kShareWaves
+                   ? launch_gu<DT, TG, VEC, EK, MODE, 2, true>(a, ntn, st)
+                   : launch_gu<DT, TG, VEC, EK, MODE, 2>(a, ntn, st);
       if (a.slots == 3)
         return a.tok_share && a.waves == kShareWaves
                    ? launch_gu<DT, TG, VEC, EK, MODE, 3, true>(a, ntn, st)
@@ -1069,6 +1093,10 @@ template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2>
 hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
   if constexpr (sizeof(DT) == 2 && VEC && EK) {
     if (a.s.I % 64 == 0) {
+      if (a.slots == 2)
+        return a.tok_share && a.waves == kShareWaves
+                   ? launch_d<DT, TG, VEC, EK, MODE, R2, 2, true>(a, ntn, st)
+                   : launch_d<DT, TG, VEC, EK, MODE, R2, 2>(a, ntn, st);
       if (a.slots == 3)
         return a.tok_share && a.waves == kShareWaves
                    ? launch_d<DT, TG, VEC, EK, MODE, R2, 3, true>(a, ntn, st)

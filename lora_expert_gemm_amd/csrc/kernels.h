@@ -69,7 +69,7 @@ struct GemmArgs {
                            // (bf16, contraction a multiple of 64); 0: loads into registers
   int ksplit;              // streaming down GEMM with the LDS ring: contraction splits, each
                            // writing its own partial y (1: none)
-  int tok_share;           // LDS ring, 4-wave workgroups, 3 slots: the block's tokens fetched
+  int tok_share;           // LDS ring, 4-wave workgroups: the block's tokens fetched
                            // once per workgroup into a shared LDS ring (0: per wave)
   int rotate;              // LDS ring: workgroups start their contraction walk at staggered
                            // slabs (weight rows a multiple of 4 KB), 0: all at slab 0
@@ -83,12 +83,13 @@ struct GemmArgs {
 
 // LDS ring slots per wave of the streaming GEMMs' weight stream (bf16 with a
 // contraction that is a multiple of 64); the launchers hold instances for
-// the counts ring_slots_supported accepts, 0 meaning loads into registers
-// (at least 3: a two-slot ring gave wrong outputs).
+// the counts ring_slots_supported accepts, 0 meaning loads into registers.
+// Two slots leave no slab of slack between a slab's wait and its reads (the
+// exactness test of the wait arithmetic); three are the measured default.
 constexpr int kRingSlots = 3;
-inline bool ring_slots_supported(int s) { return s == 0 || s == 3 || s == 4; }
+inline bool ring_slots_supported(int s) { return s == 0 || s == 2 || s == 3 || s == 4; }
 
-// Workgroups of kShareWaves waves with a 3-slot ring fetch the block's tokens
+// Workgroups of kShareWaves waves with an LDS ring fetch the block's tokens
 // once into a shared LDS ring (GemmArgs::tok_share).  Their dynamic LDS:
 // token rows table, token ring, the waves' weight rings (NW 16-row tiles
 // each).

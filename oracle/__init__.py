@@ -29,16 +29,18 @@ _LIB = os.path.join(_LIB_DIR, "libmoelora_ref.so")
 F32, BF16 = 0, 1
 
 
+_CFLAGS = ["-O2", "-fopenmp", "-std=c11", "-fPIC", "-shared"]
+
+
 def build(force=True):
-    """Compile the oracle with gcc (plain -O2: no fast-math, so every sum
-    stays sequential)."""
+    """Compile the oracle with gcc (no fast-math, so every sum stays
+    sequential; OpenMP spreads independent tokens over threads)."""
     os.makedirs(_LIB_DIR, exist_ok=True)
     if not force and os.path.exists(_LIB):
         return _LIB
     tmp = _LIB + ".tmp"
     subprocess.check_call(
-        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
-         "-o", tmp, _SRC, "-lm"])
+        ["gcc", *_CFLAGS, "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
     os.replace(tmp, _LIB)
     return _LIB
 
@@ -56,6 +58,8 @@ def _bind(path):
     lib.ref_forward.argtypes = [i, i, i, i, i, i, i, i,
                                 P, P, P, P, P, P, P, P, P, P, P, i, P]
     lib.ref_forward.restype = i
+    lib.ref_set_threads.argtypes = [i]
+    lib.ref_set_threads.restype = i
     return lib
 
 
@@ -155,6 +159,12 @@ def ref_forward(x, ids, w, adapter_ids, W_gu, W_d, A_gu=None, B_gu=None,
     return out
 
 
+def set_threads(n):
+    """Threads the oracle's forward uses (0: all, the OpenMP default);
+    returns that count.  Results do not depend on it."""
+    return int(_load().ref_set_threads(int(n)))
+
+
 class Variant:
     """The oracle's API bound to another build of the C source (used by the
     test that plants mistakes in a copy of the oracle to show the pins catch
@@ -179,8 +189,7 @@ def build_variant(src_text, so_path):
     c_path = so_path[:-3] + ".c"
     with open(c_path, "w") as f:
         f.write(src_text)
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-w",
-                           "-o", so_path, c_path, "-lm"])
+    subprocess.check_call(["gcc", *_CFLAGS, "-w", "-o", so_path, c_path, "-lm"])
     return Variant(so_path)
 
 

@@ -34,6 +34,11 @@
  * shift) and all arithmetic is double, each sum taken sequentially in
  * ascending index order.  Nothing here is rounded to bf16.
  *
+ * Threads.  ref_forward may compute different tokens on different OpenMP
+ * threads (tokens are independent; each token's arithmetic runs on one
+ * thread in the order written below), so the result does not depend on the
+ * thread count.  ref_set_threads fixes the count (0: the OpenMP default).
+ *
  * Storage (row-major, contraction dimension contiguous):
  *   x        [T][H]
  *   W_gu     [E][2I][H]     rows 0..I-1 gate, rows I..2I-1 up
@@ -46,6 +51,9 @@
  *   adapter  [T]            -1 = none
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -267,6 +275,101 @@ int ref_align(int T, int k, int E, int NA, int BM, const int32_t *ids,
  * nothing; adapter ids outside [0, NA) mean no adapter.  Null LoRA pointers
  * mean no adapter for any token.
  */
+/* One selected token's output row o[H] (see ref_forward); g, h, y, z are
+ * scratch rows of 2I, I, H and max(r, 1) doubles. */
+static void ref_token(int t, int T, int H, int I, int E, int k, int NA, int r, int dtype,
+                      int lora, const void *x, const int32_t *ids, const double *w,
+                      const int32_t *adapter_ids, const void *W_gu, const void *W_d,
+                      const void *A_gu, const void *B_gu, const void *A_d,
+                      const void *B_d, double *o, double *g, double *h, double *y,
+                      double *z)
+{
+    size_t I2 = 2 * (size_t)I;
+    for (int m = 0; m < H; ++m)
+        o[m] = 0.0;
+    if (t < 0 || t >= T)
+        return;
+    int a = lora ? adapter_ids[t] : -1;
+    if (a < 0 || a >= NA)
+        a = -1;
+    for (int j = 0; j < k; ++j) {
+        int e = ids[(size_t)t * k + j];
+        if (e < 0 || e >= E)
+            continue;
+        /* gate_up: base, then shrink and expand */
+        for (size_t n = 0; n < I2; ++n) {
+            double acc = 0.0;
+            size_t wrow = ((size_t)e * I2 + n) * H;
+            for (int c = 0; c < H; ++c)
+                acc += ld(x, (size_t)t * H + c, dtype) * ld(W_gu, wrow + c, dtype);
+            g[n] = acc;
+        }
+        if (a >= 0) {
+            size_t pair = (size_t)a * E + e;
+            for (int c = 0; c < r; ++c) {
+                double acc = 0.0;
+                size_t arow = (pair * r + c) * H;
+                for (int q = 0; q < H; ++q)
+                    acc += ld(x, (size_t)t * H + q, dtype) * ld(A_gu, arow + q, dtype);
+                z[c] = acc;
+            }
+            for (size_t n = 0; n < I2; ++n) {
+                double acc = 0.0;
+                size_t brow = (pair * I2 + n) * r;
+                for (int c = 0; c < r; ++c)
+                    acc += z[c] * ld(B_gu, brow + c, dtype);
+                g[n] += acc;
+            }
+        }
+        /* activation */
+        for (int i = 0; i < I; ++i)
+            h[i] = silu(g[i]) * g[(size_t)I + i];
+        /* down: base, then shrink and expand */
+        for (int m = 0; m < H; ++m) {
+            double acc = 0.0;
+            size_t wrow = ((size_t)e * H + m) * I;
+            for (int i = 0; i < I; ++i)
+                acc += h[i] * ld(W_d, wrow + i, dtype);
+            y[m] = acc;
+        }
+        if (a >= 0) {
+            size_t pair = (size_t)a * E + e;
+            for (int c = 0; c < r; ++c) {
+                double acc = 0.0;
+                size_t arow = (pair * r + c) * I;
+                for (int i = 0; i < I; ++i)
+                    acc += h[i] * ld(A_d, arow + i, dtype);
+                z[c] = acc;
+            }
+            for (int m = 0; m < H; ++m) {
+                double acc = 0.0;
+                size_t brow = (pair * H + m) * r;
+                for (int c = 0; c < r; ++c)
+                    acc += z[c] * ld(B_d, brow + c, dtype);
+                y[m] += acc;
+            }
+        }
+        /* routing-weighted sum over the k experts */
+        double wj = w[(size_t)t * k + j];
+        for (int m = 0; m < H; ++m)
+            o[m] += wj * y[m];
+    }
+}
+
+static int ref_threads = 0;
+
+/* Threads of ref_forward (0: the OpenMP default); returns the count a call
+ * will use. */
+int ref_set_threads(int n)
+{
+    ref_threads = n > 0 ? n : 0;
+#ifdef _OPENMP
+    return ref_threads ? ref_threads : omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 int ref_forward(int T, int H, int I, int E, int k, int NA, int r, int dtype,
                 const void *x, const int32_t *ids, const double *w,
                 const int32_t *adapter_ids, const void *W_gu, const void *W_d,
@@ -277,95 +380,33 @@ int ref_forward(int T, int H, int I, int E, int k, int NA, int r, int dtype,
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || NA < 0 || r < 0)
         return -1;
     int lora = A_gu && B_gu && A_d && B_d && adapter_ids && NA > 0 && r > 0;
-    size_t I2 = 2 * (size_t)I;
-    double *g = (double *)malloc(sizeof(double) * I2);
-    double *h = (double *)malloc(sizeof(double) * (size_t)I);
-    double *y = (double *)malloc(sizeof(double) * (size_t)H);
-    double *z = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
-    if (!g || !h || !y || !z) {
+    int nsel = tokens ? n_sel : T;
+    int fail = 0;
+#ifdef _OPENMP
+    int nt = ref_threads ? ref_threads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt) reduction(| : fail)
+#endif
+    {
+        double *g = (double *)malloc(sizeof(double) * 2 * (size_t)I);
+        double *h = (double *)malloc(sizeof(double) * (size_t)I);
+        double *y = (double *)malloc(sizeof(double) * (size_t)H);
+        double *z = (double *)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+        if (!g || !h || !y || !z)
+            fail = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int s = 0; s < nsel; ++s) {
+            if (fail)
+                continue;
+            ref_token(tokens ? tokens[s] : s, T, H, I, E, k, NA, r, dtype, lora, x, ids, w,
+                      adapter_ids, W_gu, W_d, A_gu, B_gu, A_d, B_d,
+                      out_sel + (size_t)s * H, g, h, y, z);
+        }
         free(g);
         free(h);
         free(y);
         free(z);
-        return -2;
     }
-    int nsel = tokens ? n_sel : T;
-    for (int s = 0; s < nsel; ++s) {
-        int t = tokens ? tokens[s] : s;
-        double *o = out_sel + (size_t)s * H;
-        for (int m = 0; m < H; ++m)
-            o[m] = 0.0;
-        if (t < 0 || t >= T)
-            continue;
-        int a = lora ? adapter_ids[t] : -1;
-        if (a < 0 || a >= NA)
-            a = -1;
-        for (int j = 0; j < k; ++j) {
-            int e = ids[(size_t)t * k + j];
-            if (e < 0 || e >= E)
-                continue;
-            /* gate_up: base, then shrink and expand */
-            for (size_t n = 0; n < I2; ++n) {
-                double acc = 0.0;
-                size_t wrow = ((size_t)e * I2 + n) * H;
-                for (int c = 0; c < H; ++c)
-                    acc += ld(x, (size_t)t * H + c, dtype) * ld(W_gu, wrow + c, dtype);
-                g[n] = acc;
-            }
-            if (a >= 0) {
-                size_t pair = (size_t)a * E + e;
-                for (int c = 0; c < r; ++c) {
-                    double acc = 0.0;
-                    size_t arow = (pair * r + c) * H;
-                    for (int q = 0; q < H; ++q)
-                        acc += ld(x, (size_t)t * H + q, dtype) * ld(A_gu, arow + q, dtype);
-                    z[c] = acc;
-                }
-                for (size_t n = 0; n < I2; ++n) {
-                    double acc = 0.0;
-                    size_t brow = (pair * I2 + n) * r;
-                    for (int c = 0; c < r; ++c)
-                        acc += z[c] * ld(B_gu, brow + c, dtype);
-                    g[n] += acc;
-                }
-            }
-            /* activation */
-            for (int i = 0; i < I; ++i)
-                h[i] = silu(g[i]) * g[(size_t)I + i];
-            /* down: base, then shrink and expand */
-            for (int m = 0; m < H; ++m) {
-                double acc = 0.0;
-                size_t wrow = ((size_t)e * H + m) * I;
-                for (int i = 0; i < I; ++i)
-                    acc += h[i] * ld(W_d, wrow + i, dtype);
-                y[m] = acc;
-            }
-            if (a >= 0) {
-                size_t pair = (size_t)a * E + e;
-                for (int c = 0; c < r; ++c) {
-                    double acc = 0.0;
-                    size_t arow = (pair * r + c) * I;
-                    for (int i = 0; i < I; ++i)
-                        acc += h[i] * ld(A_d, arow + i, dtype);
-                    z[c] = acc;
-                }
-                for (int m = 0; m < H; ++m) {
-                    double acc = 0.0;
-                    size_t brow = (pair * H + m) * r;
-                    for (int c = 0; c < r; ++c)
-                        acc += z[c] * ld(B_d, brow + c, dtype);
-                    y[m] += acc;
-                }
-            }
-            /* routing-weighted sum over the k experts */
-            double wj = w[(size_t)t * k + j];
-            for (int m = 0; m < H; ++m)
-                o[m] += wj * y[m];
-        }
-    }
-    free(g);
-    free(h);
-    free(y);
-    free(z);
-    return 0;
+    return fail ? -2 : 0;
 }

@@ -287,3 +287,19 @@ def test_bf16_inputs_widen_exactly(oracle_lib):
                                dtype=oracle_lib.BF16)
     b = run_oracle(oracle_lib, df, w, ids, wts)
     assert np.array_equal(a, b)
+
+
+def test_thread_count_does_not_change_results():
+    """Tokens are independent and each is computed by one thread in the
+    written order, so one thread and all threads agree bit for bit."""
+    import oracle
+    w, d = small_workload(T=23, H=24, I=20, E=5, k=3, NA=3, r=4)
+    ids, wts = oracle.ref_route(d["logits"], w.k)
+    try:
+        oracle.set_threads(1)
+        one = run_oracle(oracle, d, w, ids, wts)
+        assert oracle.set_threads(0) >= 1
+        many = run_oracle(oracle, d, w, ids, wts)
+    finally:
+        oracle.set_threads(0)
+    assert np.array_equal(one, many)
