@@ -71,7 +71,9 @@ typedef enum moelora_status {
     MOELORA_ERR_UNSUPPORTED = -2,  /* shape or dtype outside the limits    */
     MOELORA_ERR_WORKSPACE = -3,    /* workspace too small                  */
     MOELORA_ERR_HIP = -4,          /* a HIP runtime call or launch failed  */
-    MOELORA_ERR_DEVICE = -5        /* the device error word is non-zero    */
+    MOELORA_ERR_DEVICE = -5,       /* the device error word is non-zero    */
+    MOELORA_ERR_TOO_LARGE = -6     /* beyond moelora_forward_noalloc's
+                                      static scratch buffer                */
 } moelora_status;
 
 typedef enum moelora_dtype { MOELORA_F32 = 0, MOELORA_BF16 = 1 } moelora_dtype;
@@ -162,6 +164,31 @@ MOELORA_API moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens
                                void *out, void *workspace,
                                size_t workspace_bytes,
                                moelora_stream_t stream);
+
+/* moelora_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments and results as moelora_forward, without the
+ * workspace: the call uses a static device array of the library,
+ * MOELORA_STATIC_SCRATCH_BYTES (64 MiB) per GPU, allocated with the
+ * library's code on each GPU it runs on and held until the process ends.
+ * The call allocates nothing; its first call on a GPU looks up that GPU's
+ * copy of the array.  `stream` must belong to the current device
+ * (else MOELORA_ERR_INVALID_ARG).  A call whose workspace (the size
+ * moelora_plan_info reports for n_tokens) exceeds the array returns
+ * MOELORA_ERR_TOO_LARGE before touching the device.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (two streams, two
+ * threads) race and must be serialised by the caller, e.g. on one stream.
+ * The array's contents need no initialisation; moelora_read_device_error
+ * does not apply (its error word lives in the array). */
+#define MOELORA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+MOELORA_API moelora_status moelora_forward_noalloc(moelora_plan_t plan, int32_t n_tokens,
+                               const void *x, const float *router_logits,
+                               const int32_t *topk_ids, const float *topk_w,
+                               const int32_t *adapter_ids,
+                               const void *w_gate_up, const void *w_down,
+                               const void *lora_a_gu, const void *lora_b_gu,
+                               const void *lora_a_d, const void *lora_b_d,
+                               void *out, moelora_stream_t stream);
 
 MOELORA_API const char *moelora_status_string(moelora_status status);
 

@@ -5,7 +5,7 @@ function here has the name of the C entry point it calls and only converts
 arguments (tensors to device pointers, status codes to exceptions).  All of
 the layer's work runs in the library's HIP kernels; there is no fallback.
 Importing this package fails loudly when ``_lib/libmoelora.so`` has not been
-built (``python -m lora_expert_gemm_amd.build``).
+built (``python lora_expert_gemm_amd/build.py``).
 
 Tensor arguments may be torch tensors (their ``data_ptr()`` is passed), raw
 integer addresses, or None for a null pointer.
@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moelora.h")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m lora_expert_gemm_amd.build)")
+        "(python lora_expert_gemm_amd/build.py)")
 
 # One HIP runtime per process.  PyTorch for ROCm ships its own libamdhip64
 # (requested by the unversioned name libamdhip64.so); this library requests
@@ -37,6 +37,8 @@ except ImportError:
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE = 0, -1, -2, -3, -4, -5
+ERR_TOO_LARGE = -6
+STATIC_SCRATCH_BYTES = 64 << 20
 F32, BF16 = 0, 1
 DEVERR_EXPERT_ID, DEVERR_ADAPTER_ID = 1, 2
 FLAG_DETERMINISTIC, FLAG_DEBUG_CHECK_IDS = 1, 2
@@ -70,6 +72,8 @@ _lib.moelora_plan_destroy.argtypes = [_P]
 _lib.moelora_plan_destroy.restype = None
 _lib.moelora_forward.argtypes = [_P, _I32] + [_P] * 13 + [ctypes.c_size_t, _P]
 _lib.moelora_forward.restype = ctypes.c_int
+_lib.moelora_forward_noalloc.argtypes = [_P, _I32] + [_P] * 12 + [_P]
+_lib.moelora_forward_noalloc.restype = ctypes.c_int
 _lib.moelora_status_string.argtypes = [ctypes.c_int]
 _lib.moelora_status_string.restype = ctypes.c_char_p
 _lib.moelora_workspace_layout.argtypes = [_P, _I32, ctypes.POINTER(moelora_layout)]
@@ -148,6 +152,16 @@ def moelora_forward(plan, n_tokens, x, router_logits, topk_ids, topk_w, adapter_
         _ptr(adapter_ids), _ptr(w_gate_up), _ptr(w_down), _ptr(lora_a_gu),
         _ptr(lora_b_gu), _ptr(lora_a_d), _ptr(lora_b_d), _ptr(out), _ptr(workspace),
         workspace_bytes, _stream(stream)), "moelora_forward")
+
+
+def moelora_forward_noalloc(plan, n_tokens, x, router_logits, topk_ids, topk_w, adapter_ids,
+                            w_gate_up, w_down, lora_a_gu, lora_b_gu, lora_a_d, lora_b_d,
+                            out, stream=None):
+    _check(_lib.moelora_forward_noalloc(
+        plan, n_tokens, _ptr(x), _ptr(router_logits), _ptr(topk_ids), _ptr(topk_w),
+        _ptr(adapter_ids), _ptr(w_gate_up), _ptr(w_down), _ptr(lora_a_gu),
+        _ptr(lora_b_gu), _ptr(lora_a_d), _ptr(lora_b_d), _ptr(out), _stream(stream)),
+        "moelora_forward_noalloc")
 
 
 def moelora_workspace_layout(plan, n_tokens):

@@ -18,6 +18,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -317,6 +319,7 @@ const char *moelora_status_string(moelora_status st) {
     case MOELORA_ERR_WORKSPACE: return "workspace too small";
     case MOELORA_ERR_HIP: return "HIP runtime error";
     case MOELORA_ERR_DEVICE: return "device error word set";
+    case MOELORA_ERR_TOO_LARGE: return "call needs more than the static scratch buffer holds";
   }
   return "unknown status";
 }
@@ -429,13 +432,20 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   return MOELORA_OK;
 }
 
-moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void *x,
-                               const float *router_logits, const int32_t *topk_ids,
-                               const float *topk_w, const int32_t *adapter_ids,
-                               const void *w_gate_up, const void *w_down, const void *lora_a_gu,
-                               const void *lora_b_gu, const void *lora_a_d, const void *lora_b_d,
-                               void *out, void *workspace, size_t workspace_bytes,
-                               moelora_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer call behind both forward entry points: `workspace` is the
+// caller's buffer (moelora_forward) or this device's static scratch array
+// (moelora_forward_noalloc).
+moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x,
+                            const float *router_logits, const int32_t *topk_ids,
+                            const float *topk_w, const int32_t *adapter_ids,
+                            const void *w_gate_up, const void *w_down, const void *lora_a_gu,
+                            const void *lora_b_gu, const void *lora_a_d, const void *lora_b_d,
+                            void *out, void *workspace, size_t workspace_bytes,
+                            moelora_stream_t stream) {
   if (!plan) return MOELORA_ERR_INVALID_ARG;
   const moelora_desc &d = plan->d;
   if (n_tokens < 0 || n_tokens > d.max_tokens) return MOELORA_ERR_INVALID_ARG;
@@ -600,6 +610,77 @@ moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void
   MOELORA_TRY(mark());
 #undef MOELORA_TRY
   return MOELORA_OK;
+}
+
+// Allocation-free calls: the workspace lives in a file-scope device array.
+// Each GPU the library runs on holds its own copy (from the first call on it
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// not device memory, so its device address is looked up once per device
+// with hipGetSymbolAddress and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The device address of this device's scratch array (looked up on the
+// first call on the device, with that device current).
+moelora_status static_scratch(hipStream_t st, void **ptr) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MOELORA_ERR_HIP;
+  if (hipStreamGetDevice(st, &dev) != hipSuccess) return MOELORA_ERR_HIP;
+  // the address belongs to the current device: the stream must run there
+  if (dev != cur) return MOELORA_ERR_INVALID_ARG;
+  if (cur < 0 || cur >= kMaxDevices) return MOELORA_ERR_UNSUPPORTED;
+  void *p = g_scratch_ptr[cur].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[cur].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOELORA_ERR_HIP;
+      g_scratch_ptr[cur].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return MOELORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moelora_status moelora_forward(moelora_plan_t plan, int32_t n_tokens, const void *x,
+                               const float *router_logits, const int32_t *topk_ids,
+                               const float *topk_w, const int32_t *adapter_ids,
+                               const void *w_gate_up, const void *w_down, const void *lora_a_gu,
+                               const void *lora_b_gu, const void *lora_a_d, const void *lora_b_d,
+                               void *out, void *workspace, size_t workspace_bytes,
+                               moelora_stream_t stream) {
+  return forward_impl(plan, n_tokens, x, router_logits, topk_ids, topk_w, adapter_ids, w_gate_up,
+                      w_down, lora_a_gu, lora_b_gu, lora_a_d, lora_b_d, out, workspace,
+                      workspace_bytes, stream);
+}
+
+moelora_status moelora_forward_noalloc(moelora_plan_t plan, int32_t n_tokens, const void *x,
+                                       const float *router_logits, const int32_t *topk_ids,
+                                       const float *topk_w, const int32_t *adapter_ids,
+                                       const void *w_gate_up, const void *w_down,
+                                       const void *lora_a_gu, const void *lora_b_gu,
+                                       const void *lora_a_d, const void *lora_b_d, void *out,
+                                       moelora_stream_t stream) {
+  if (!plan) return MOELORA_ERR_INVALID_ARG;
+  if (n_tokens < 0 || n_tokens > plan->d.max_tokens) return MOELORA_ERR_INVALID_ARG;
+  if (n_tokens == 0) return MOELORA_OK;
+  // the size check comes before any device call
+  if (make_layout(plan->d, plan->tune, n_tokens).total > kStaticScratchBytes)
+    return MOELORA_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  const moelora_status st = static_scratch(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (st != MOELORA_OK) return st;
+  return forward_impl(plan, n_tokens, x, router_logits, topk_ids, topk_w, adapter_ids, w_gate_up,
+                      w_down, lora_a_gu, lora_b_gu, lora_a_d, lora_b_d, out, ws,
+                      kStaticScratchBytes, stream);
 }
 
 moelora_status moelora_read_device_error(moelora_plan_t plan, const void *workspace,

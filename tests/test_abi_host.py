@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert lib.moelora_status_string(st) != "unknown status"
 
 

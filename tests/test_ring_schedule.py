@@ -247,7 +247,7 @@ ASM = os.path.join(BUILD, "expert_gemm-gfx950.s")
 
 
 @pytest.mark.skipif(not os.path.exists(ASM), reason="device assembly not built "
-                    "(python -m lora_expert_gemm_amd.build)")
+                    "(python lora_expert_gemm_amd/build.py)")
 def test_compiled_ring_loops_issue_what_their_waits_count():
     text = open(ASM).read()
     seen = {2: 0, 3: 0, 4: 0}
