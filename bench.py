@@ -5,7 +5,12 @@ expand + SiLU*up, down shrink, down GEMM + expand, top-k combine) on one
 batch of seeded synthetic input already resident in HBM.  Prints one JSON
 line with tokens/s, the roofline of the dominant kernel (timed live with
 HIP events on the stream it runs on) and the CPU oracle's rate on a bounded
-sample of the same workload.
+sample of the same workload, single-threaded and on all host cores.
+
+The headline metric has two halves: HBM bandwidth for decode-sized batches
+(the default workload, whose tokens/s is `value`) and MFMA utilisation for
+prefill-sized batches; the default run therefore also times the 6400-token
+prefill workload and reports it as the nested `prefill` object.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 """
@@ -49,6 +54,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--prefill-steps", type=int, default=20,
+                    help="timed calls of the prefill leg (0: no prefill leg)")
+    ap.add_argument("--prefill-warmup", type=int, default=5)
     return ap.parse_args()
 
 
@@ -144,11 +152,24 @@ def copy_calibration(mib):
     log(f"copy calibration: 5 copies of {n} bytes")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, d, target_s):
-    """The oracle (single thread, float64) on a bounded sample of the
-    workload: its first n tokens, n chosen so the run takes about target_s
-    seconds; when the whole workload is quicker than that, whole passes
-    are repeated until target_s is reached."""
+    """The oracle (float64 C) on a bounded sample of the workload, once on one
+    thread and once on every thread OpenMP gives it (tokens spread over
+    threads, each token's arithmetic unchanged): its first n tokens, n
+    chosen so each run takes about target_s / 2 seconds; when the whole
+    workload is quicker than that, whole passes are repeated.  `value` and
+    `cores` are the all-thread run's."""
     import oracle
     dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
     ids, wts = oracle.ref_route(d["logits"], w.k)
@@ -160,48 +181,65 @@ def cpu_baseline(w, d, target_s):
                            n_adapters=w.NA, dtype=dt, tokens=np.asarray(tokens, np.int32))
         return time.perf_counter() - t0
 
-    t1 = run([0])
-    n = int(max(1, min(w.T, target_s / max(t1, 1e-6))))
-    el, passes = 0.0, 0
-    while passes == 0 or (n == w.T and el < target_s):
-        el += run(list(range(n)))
-        passes += 1
-    what = f"tokens 0..{n - 1} of {w.T}" if n < w.T else f"all {w.T} tokens x {passes} passes"
-    return {"value": n * passes / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle (C, float64, 1 thread) on {what} of {w.name}; {el:.1f} s"}
+    def timed(threads, budget):
+        used = oracle.set_threads(threads)
+        t1 = run(list(range(min(w.T, used))))
+        per_tok = t1 / min(w.T, used) * used   # one token's time on one thread
+        n = int(max(1, min(w.T, budget / max(per_tok, 1e-6) * used)))
+        el, passes = 0.0, 0
+        while passes == 0 or (n == w.T and el < budget):
+            el += run(list(range(n)))
+            passes += 1
+        what = f"tokens 0..{n - 1} of {w.T}" if n < w.T else f"all {w.T} tokens x {passes} passes"
+        return used, n * passes / el, f"{what} of {w.name}; {el:.1f} s"
+
+    try:
+        _, v1, s1 = timed(1, target_s / 2)
+        used, vn, sn = timed(0, target_s / 2)
+    finally:
+        oracle.set_threads(0)
+    return {"value": vn, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"oracle (C, float64, OpenMP over tokens, {used} threads) on {sn}",
+            "single_thread": {"value": v1, "cores": 1,
+                              "sample": f"oracle (C, float64, 1 thread) on {s1}"},
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
 
 
 def ceilings(torch, stream):
-    """What the same device reaches on plain work, timed here for context:
-    a 1 GiB device copy (bytes read + written per second) and a bf16
-    8192^3 torch.matmul (the vendor GEMM library)."""
+    """What the same device reaches on plain work, timed here for context: a
+    read-only stream (the vendor bf16 GEMV, torch.mv, over a 2 GiB matrix of
+    131072 x 8192: bytes read per second; it out-streams torch's
+    reductions, which reach 3.7-5.6 TB/s on the same bytes), a 1 GiB device
+    copy (bytes read + written per second) and a bf16 8192^3 torch.matmul
+    (the vendor GEMM)."""
     res = {}
-    try:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, n, bytes_per):
         for _ in range(3):
-            b.copy_(a)
+            fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(10):
-            b.copy_(a)
+        for _ in range(n):
+            fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        res["copy_GB/s"] = 2 * a.numel() * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+        return bytes_per * n / (e0.elapsed_time(e1) / 1e3)
+
+    try:
+        m = torch.ones((1 << 17, 8192), dtype=torch.bfloat16, device="cuda")   # 2 GiB
+        v = torch.ones(8192, dtype=torch.bfloat16, device="cuda")
+        res["read_GB/s"] = rate(lambda: torch.mv(m, v), 10, m.numel() * 2) / 1e9
+        del m, v
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        res["copy_GB/s"] = rate(lambda: b.copy_(a), 10, 2 * a.numel()) / 1e9
         del a, b
         n = 8192
         x = torch.randn(n, n, device="cuda").to(torch.bfloat16)
         y = torch.randn(n, n, device="cuda").to(torch.bfloat16)
-        for _ in range(3):
-            torch.matmul(x, y)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(10):
-            torch.matmul(x, y)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res["gemm_bf16_TFLOP/s"] = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
+        res["gemm_bf16_TFLOP/s"] = rate(lambda: torch.matmul(x, y), 10, 2 * n ** 3) / 1e12
         del x, y
     except Exception as ex:  # context only
         res["error"] = str(ex)
@@ -236,26 +274,17 @@ def graph_replay(torch, step, stream, steps):
         return {"ms_per_step": None, "error": str(ex)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        log(f"bench.py measures one GPU only (this build has no multi-GPU path); "
-            f"--gpus {args.gpus} is not supported")
-        sys.exit(2)
-    import torch
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_calib:
-        copy_calibration(args.copy_calib)
-        return
-    import lora_expert_gemm_amd as L
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-
-    w = synth.workload(args.workload)
+def measure(torch, L, w, steps, warmup, no_lora=False, graph_steps=None):
+    """Time `steps` layer calls of workload w (after `warmup`), then the same
+    calls with the library's per-stage events and as a hipGraph replay;
+    returns the timings, the algorithmic counts of the call and the roofline
+    of its dominant kernel."""
     log(f"[bench] generating {w}")
     d = synth.make_inputs(w)
     dtype = L.BF16 if w.dtype == "bf16" else L.F32
     plan = L.Plan(w.T, w.H, w.I, w.E, w.k, w.NA, w.r, dtype)
-    log(f"[bench] plan: {plan.info(w.T)}")
+    info = plan.info(w.T)
+    log(f"[bench] plan: {info}")
 
     def dev(a):
         a = a.view(np.int16) if a.dtype == np.uint16 else a
@@ -266,97 +295,144 @@ def main():
     out = torch.empty((w.T, w.H), dtype=torch.int16 if w.dtype == "bf16" else torch.float32,
                       device="cuda")
     stream = torch.cuda.current_stream()
-
-    lora = [None] * 4 if args.no_lora else [t["A_gu"], t["B_gu"], t["A_d"], t["B_d"]]
+    lora = [None] * 4 if no_lora else [t["A_gu"], t["B_gu"], t["A_d"], t["B_d"]]
 
     def step(st=None):
         L.moelora_forward(plan.handle, w.T, t["x"], t["logits"], None, None, t["adapter_ids"],
                           t["W_gu"], t["W_d"], *lora, out, ws, plan.workspace_bytes,
                           (st or stream).cuda_stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
+    ms = ev0.elapsed_time(ev1) / steps
+    log(f"[bench] {w.name}: {steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")
 
     # per-stage times: events recorded by the library around each kernel
     # stage on the forward's own stream
-    L.moelora_timing_begin(plan.handle, args.steps)
-    for _ in range(args.steps):
+    L.moelora_timing_begin(plan.handle, steps)
+    for _ in range(steps):
         step()
     st_ms, n_calls = L.moelora_timing_end(plan.handle)
     stage = {n: v / n_calls for n, v in zip(STAGES, st_ms)}
     log("[bench] stages (ms/call): " + ", ".join(f"{n}={v:.4f}" for n, v in stage.items()))
-
-    graph = graph_replay(torch, step, stream, args.steps)
-    ceil = ceilings(torch, stream)
+    graph = graph_replay(torch, step, stream, graph_steps or steps)
 
     lay = plan.layout(w.T)
     torch.cuda.synchronize()
     ids = ws[lay["off_topk_ids"]: lay["off_topk_ids"] + 4 * w.T * w.k].cpu().numpy() \
         .view(np.int32).reshape(w.T, w.k)
-    alg = algorithmic(w, ids, d["adapter_ids"] if not args.no_lora
-                      else np.full(w.T, -1, np.int32), "lora_mode=row" in plan.info(w.T))
-
+    alg = algorithmic(w, ids, d["adapter_ids"] if not no_lora else np.full(w.T, -1, np.int32),
+                      "lora_mode=row" in info)
     dom = max(("gate_up", "down"), key=lambda n: stage[n])
-    dom_s = stage[dom] / 1e3
-    decode = hbm_bound(alg, dom, w.dtype)
-    if decode:
-        roof = {"bound": "hbm", "kernel": dom, "achieved": alg[f"{dom}_bytes"] / dom_s / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "kernel": dom, "achieved": alg[f"{dom}_flop"] / dom_s / 1e12,
-                "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    ref = ceil.get("copy_GB/s" if decode else "gemm_bf16_TFLOP/s")
-    roof["frac_of_measured_ceiling"] = roof["achieved"] / ref if ref else None
-    roof["traffic"] = None if args.no_lora else measured_traffic(w.name, dom)
-    roof["launch_ms"] = stage[dom]
-    roof["units_per_launch"] = {"experts": alg["n_exp"], "adapter_expert_pairs": alg["n_pair"],
-                                "routed_rows": alg["R"]}
-
+    roof = {**roofline(alg, dom, stage[dom], w.dtype), "kernel": dom,
+            "traffic": None if no_lora else measured_traffic(w.name, dom),
+            "launch_ms": stage[dom],
+            "units_per_launch": {"experts": alg["n_exp"], "adapter_expert_pairs": alg["n_pair"],
+                                 "routed_rows": alg["R"]}}
     layer_s = ms / 1e3
+    layer = {"algo_bytes": alg["layer_bytes"], "algo_flop": alg["layer_flop"],
+             "GB/s": alg["layer_bytes"] / layer_s / 1e9,
+             "TFLOP/s": alg["layer_flop"] / layer_s / 1e12,
+             "hbm_frac": alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS,
+             "mfma_frac": alg["layer_flop"] / layer_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]}
+    kernels = {k: roofline(alg, k, stage[k], w.dtype) for k in ("gate_up", "down") if stage[k] > 0}
+    del t, ws, out
+    return dict(w=w, d=d, ms=ms, stage=stage, graph=graph, alg=alg, roof=roof, layer=layer,
+                kernels=kernels, plan=info)
+
+
+def roofline(alg, kernel, launch_ms, dtype):
+    """Achieved rate of one kernel against the roofline its algorithmic
+    intensity puts it under (HBM bytes, or MFMA FLOPs of the layer dtype)."""
+    sec = launch_ms / 1e3
+    if hbm_bound(alg, kernel, dtype):
+        r = {"bound": "hbm", "achieved": alg[f"{kernel}_bytes"] / sec / 1e9,
+             "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        r = {"bound": "mfma", "achieved": alg[f"{kernel}_flop"] / sec / 1e12,
+             "peak": MFMA_PEAK_TFLOPS[dtype], "unit": "TFLOP/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    return r
+
+
+def config_of(w, no_lora=False):
+    return {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.k,
+            "adapters": w.NA, "rank": w.r,
+            "adapter_ids": "none (no LoRA)" if no_lora else w.adapters}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only (every box here has one GPU and this build "
+            f"has no multi-GPU path); --gpus {args.gpus} is not supported")
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
+        return
+    import lora_expert_gemm_amd as L
+
+    w = synth.workload(args.workload)
+    m = measure(torch, L, w, args.steps, args.warmup, args.no_lora)
+    ceil = ceilings(torch, torch.cuda.current_stream())
+    roof = m["roof"]
+    ref = ceil.get("read_GB/s" if roof["bound"] == "hbm" else "gemm_bf16_TFLOP/s")
+    roof["frac_of_measured_ceiling"] = roof["achieved"] / ref if ref else None
     res = {
         "metric": METRIC,
-        "value": w.T / layer_s,
+        "value": w.T / (m["ms"] / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": m["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "top_k": w.k,
-                   "adapters": w.NA, "rank": w.r,
-                   "adapter_ids": "none (no LoRA)" if args.no_lora else w.adapters},
+        "config": config_of(w, args.no_lora),
         "roofline": roof,
-        "layer": {"algo_bytes": alg["layer_bytes"], "algo_flop": alg["layer_flop"],
-                  "GB/s": alg["layer_bytes"] / layer_s / 1e9,
-                  "TFLOP/s": alg["layer_flop"] / layer_s / 1e12,
-                  "hbm_frac": alg["layer_bytes"] / layer_s / 1e9 / HBM_PEAK_GBS},
-        "stages_ms": stage,
-        "graph": graph,
+        "layer": m["layer"],
+        "kernels": m["kernels"],
+        "stages_ms": m["stage"],
+        "graph": m["graph"],
         "ceilings": ceil,
-        "plan": plan.info(w.T),
+        "plan": m["plan"],
         "kernel_source": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        res["cpu_baseline"] = cpu_baseline(w, d, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, m["d"], args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+    del m
+    if args.workload == DEFAULT_WORKLOAD and args.prefill_steps > 0 and not args.no_lora:
+        # the metric's other half: MFMA utilisation of the prefill-sized batch
+        pw = synth.workload("prefill_bf16")
+        p = measure(torch, L, pw, args.prefill_steps, args.prefill_warmup)
+        pr = p["roof"]
+        pr["frac_of_measured_ceiling"] = (pr["achieved"] / ceil["gemm_bf16_TFLOP/s"]
+                                          if ceil.get("gemm_bf16_TFLOP/s") else None)
+        res["prefill"] = {
+            "config": config_of(pw), "steps": args.prefill_steps,
+            "warmup": args.prefill_warmup, "ms_per_step": p["ms"],
+            "tokens_per_s": pw.T / (p["ms"] / 1e3), "roofline": pr, "layer": p["layer"],
+            "kernels": p["kernels"], "stages_ms": p["stage"], "graph": p["graph"],
+            "plan": p["plan"]}
+        log(f"[bench] prefill: {p['ms']:.4f} ms/step, gate_up {pr['achieved']:.0f} TFLOP/s "
+            f"({pr['frac']:.3f} of peak), layer {p['layer']['mfma_frac']:.3f} of MFMA peak")
     print(json.dumps(res), flush=True)
 
 
