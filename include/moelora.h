@@ -38,8 +38,13 @@
  * Ownership: the caller allocates and owns every device buffer, the
  * workspace and the stream.  The library owns only the plan (a host
  * object).  moelora_forward only enqueues kernels on the given stream: it
- * never synchronises, allocates or loads code, so it can be captured in a
- * HIP graph, and nothing is specialised on the token count.
+ * never synchronises or allocates, so it can be captured in a HIP graph, and
+ * nothing is specialised on the token count.  Kernels are compiled ahead of
+ * time; the HIP runtime loads their code on first use, so the first forward
+ * of a plan on a device (the current device) looks up every kernel that
+ * plan can launch at any token count up to max_tokens, and no later forward
+ * loads code ([AWS] "Execution optimizations": loading code for each new
+ * context length cost a tenfold time-to-first-token regression).
  *
  * Errors: every entry point returns a status; nothing throws or aborts
  * across the ABI.  Device-resident ids are preconditions: expert ids in

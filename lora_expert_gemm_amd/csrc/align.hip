@@ -824,9 +824,8 @@ template <int SLOTS, typename DT>
 hipError_t launch_small(const Shape &s, const float *logits, const int *ids, int *ids_ws,
                         float *w_ws, const int *adapter_ids, const AlignBufs &al,
                         const RowShrinkArgs &rs, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_route_align_small<SLOTS, DT>), dim3(grid), dim3(kAlignThreads), 0, st, s,
-                     logits, ids, ids_ws, w_ws, adapter_ids, al, rs);
-  return hipGetLastError();
+  return launch_kernel(k_route_align_small<SLOTS, DT>, dim3(grid), dim3(kAlignThreads), 0, st, s,
+                       logits, ids, ids_ws, w_ws, adapter_ids, al, rs);
 }
 
 template <int SLOTS>
@@ -845,18 +844,16 @@ hipError_t launch_route_align_t(const Shape &s, const float *logits, const int *
   }
   if (rs) return hipErrorInvalidValue;  // row shrinks ride along with small batches only
   if (logits) {
-    hipLaunchKernelGGL(k_route<SLOTS>, dim3((s.T + 3) / 4), dim3(256), 0, st, logits, s.T, s.E,
-                       s.k, ids_ws, w_ws);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(k_route<SLOTS>, dim3((s.T + 3) / 4), dim3(256), 0, st, logits,
+                                 s.T, s.E, s.k, ids_ws, w_ws);
     if (e != hipSuccess) return e;
     ids = ids_ws;
   }
-  hipLaunchKernelGGL(k_align_meta, dim3(1), dim3(kAlignThreads), 0, st, s, ids, adapter_ids, al);
-  hipError_t e = hipGetLastError();
+  hipError_t e =
+      launch_kernel(k_align_meta, dim3(1), dim3(kAlignThreads), 0, st, s, ids, adapter_ids, al);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_align_scatter, dim3(s.E * (s.NA + 1)), dim3(kScatterThreads), 0, st, s,
-                     ids, al);
-  return hipGetLastError();
+  return launch_kernel(k_align_scatter, dim3(s.E * (s.NA + 1)), dim3(kScatterThreads), 0, st, s,
+                       ids, al);
 }
 
 }  // namespace

@@ -28,6 +28,8 @@
 
 using namespace moelora;
 
+thread_local bool moelora::tl_resolve_only = false;
+
 // Tuning switches, read from the environment once, by moelora_plan, and
 // fixed for the plan's lifetime (a forward never reads the environment).
 struct Tuning {
@@ -37,10 +39,28 @@ struct Tuning {
   bool verbose = false;    // a failed launch prints its name and HIP error to stderr
 };
 
+// What selects the kernels a forward launches, besides the call's own
+// options (LoRA or not; router or caller ids).
+struct Selection {
+  int BM, waves_gu, waves_d, down_rows, shrink_waves;
+  bool row, small_align;
+  bool operator==(const Selection &o) const {
+    return BM == o.BM && waves_gu == o.waves_gu && waves_d == o.waves_d &&
+           down_rows == o.down_rows && shrink_waves == o.shrink_waves && row == o.row &&
+           small_align == o.small_align;
+  }
+};
+
 struct moelora_plan_s {
   moelora_desc d;
   size_t ws_bytes;
   Tuning tune;
+  // every distinct selection over the token counts 1..max_tokens, with the
+  // first token count that makes it; the devices whose code for all of them
+  // has been resolved (bit per device), and the lock of that resolution
+  std::vector<std::pair<Selection, int>> selections;
+  std::atomic<uint64_t> resolved{0};
+  std::mutex resolve_mu;
   int waves_override_gu = 0, waves_override_d = 0;  // 0: the table's choice
   int down_rows = 0;  // streaming down GEMM: weight rows per wave (0: by bucket)
   int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
@@ -292,6 +312,19 @@ bool use_row_mode(const Shape &s, bool lora, int waves_d) {
   return 64 * waves_d >= rp;  // 64 threads per wave
 }
 
+// The kernel selection a forward of layout L makes (given LoRA).
+Selection selection_of(const moelora_plan_s *p, const Layout &L) {
+  Selection sel;
+  sel.BM = L.s.BM;
+  sel.waves_gu = p->waves_override_gu ? p->waves_override_gu : L.waves_gu;
+  sel.waves_d = p->waves_override_d ? p->waves_override_d : L.waves_d;
+  sel.down_rows = p->down_rows ? p->down_rows : L.down_rows;
+  sel.shrink_waves = p->shrink_waves ? p->shrink_waves : choose_shrink_waves(L.s, L.split);
+  sel.row = use_row_mode(L.s, true, sel.waves_d);
+  sel.small_align = L.s.R <= kSmallRows;
+  return sel;
+}
+
 int k_tail(const moelora_desc &d, int K) {
   const int ks = d.dtype == MOELORA_BF16 ? 32 : 16;
   return (ks - K % ks) % ks;
@@ -344,13 +377,6 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
     const int k = atoi(v);
     if (k >= 1 && k <= 8) p->tune.ksplit_d = k;
   }
-  // The largest layout over every token count up to max_tokens.  Sizes are
-  // not monotone in T (the shrink and down-GEMM split counts fall as T
-  // grows, and the block size changes between buckets), so every T is
-  // visited: make_layout is a few dozen integer operations.
-  size_t ws = make_layout(p->d, p->tune, 0).total;
-  for (int T = 1; T <= p->d.max_tokens; ++T) ws = std::max(ws, make_layout(p->d, p->tune, T).total);
-  p->ws_bytes = ws;
   // tuning sweeps only: force the waves per GEMM workgroup (1..4)
   if (const char *v = getenv("MOELORA_WAVES_GU")) p->waves_override_gu = std::max(0, std::min(4, atoi(v)));
   if (const char *v = getenv("MOELORA_WAVES_D")) p->waves_override_d = std::max(0, std::min(4, atoi(v)));
@@ -362,6 +388,22 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
   if (const char *v = getenv("MOELORA_ROTATE")) p->rotate = atoi(v) != 0;
   if (const char *v = getenv("MOELORA_SHRINK_WAVES"))
     p->shrink_waves = atoi(v) == 4 || atoi(v) == 8 || atoi(v) == kShrinkWaves ? atoi(v) : 0;
+  // The largest layout over every token count up to max_tokens.  Sizes are
+  // not monotone in T (the shrink and down-GEMM split counts fall as T
+  // grows, and the block size changes between buckets), so every T is
+  // visited: make_layout is a few dozen integer operations.  The same scan
+  // records which kernel selections the token counts make.
+  size_t ws = make_layout(p->d, p->tune, 0).total;
+  for (int T = 1; T <= p->d.max_tokens; ++T) {
+    const Layout L = make_layout(p->d, p->tune, T);
+    ws = std::max(ws, L.total);
+    const Selection sel = selection_of(p, L);
+    if (std::find_if(p->selections.begin(), p->selections.end(),
+                     [&](const std::pair<Selection, int> &e) { return e.first == sel; }) ==
+        p->selections.end())
+      p->selections.emplace_back(sel, T);
+  }
+  p->ws_bytes = ws;
   *plan = p;
   *workspace_bytes = ws;
   return MOELORA_OK;
@@ -439,6 +481,8 @@ namespace {
 // The layer call behind both forward entry points: `workspace` is the
 // caller's buffer (moelora_forward) or this device's static scratch array
 // (moelora_forward_noalloc).
+moelora_status resolve_kernels(moelora_plan_t plan);
+
 moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x,
                             const float *router_logits, const int32_t *topk_ids,
                             const float *topk_w, const int32_t *adapter_ids,
@@ -490,7 +534,7 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
   // are not free on the device timeline).
   hipEvent_t *ev = nullptr;
   unsigned *rec = nullptr;
-  if (plan->timing && plan->n_calls < plan->max_calls) {
+  if (plan->timing && plan->n_calls < plan->max_calls && !tl_resolve_only) {
     rec = &plan->recorded[plan->n_calls];
     ev = &plan->ev[(size_t)plan->n_calls++ * (MOELORA_N_STAGES + 1)];
     *rec = 0;
@@ -517,6 +561,11 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
   float *z_d = reinterpret_cast<float *>(ws + L.off_zd);
   void *h = ws + L.off_h;
 
+  // (after every host-side check: a rejected call touches no device)
+  if (!tl_resolve_only) {
+    const moelora_status rs = resolve_kernels(plan);
+    if (rs != MOELORA_OK) return rs;
+  }
   (void)hipGetLastError();  // an error left pending by an earlier call is not this call's
   MOELORA_TRY(mark());
   int *ids_ws = reinterpret_cast<int *>(ws + L.off_ids);
@@ -610,6 +659,39 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
   MOELORA_TRY(mark());
 #undef MOELORA_TRY
   return MOELORA_OK;
+}
+
+// Resolve, on the current device, every kernel a forward of this plan can
+// launch at any token count, once per device: the dispatch of forward_impl
+// runs for each recorded selection, with and without LoRA, from logits and
+// from caller ids, with tl_resolve_only set, so its launch sites look their
+// kernels up (loading code objects) and launch nothing.  The pointers are
+// never dereferenced.
+moelora_status resolve_kernels(moelora_plan_t plan) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOELORA_ERR_HIP;
+  const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;
+  if (bit && (plan->resolved.load(std::memory_order_acquire) & bit)) return MOELORA_OK;
+  std::lock_guard<std::mutex> lock(plan->resolve_mu);
+  if (bit && (plan->resolved.load(std::memory_order_acquire) & bit)) return MOELORA_OK;
+  void *const f = reinterpret_cast<void *>(uintptr_t{1} << 12);  // aligned, never dereferenced
+  const float *ff = static_cast<const float *>(f);
+  const int32_t *fi = static_cast<const int32_t *>(f);
+  moelora_status st = MOELORA_OK;
+  tl_resolve_only = true;
+  for (const auto &e : plan->selections) {
+    for (int lora = 0; lora < 2 && st == MOELORA_OK; ++lora)
+      for (int route = 0; route < 2 && st == MOELORA_OK; ++route) {
+        const void *lp = lora ? f : nullptr;
+        st = forward_impl(plan, e.second, f, route ? ff : nullptr, route ? nullptr : fi,
+                          route ? nullptr : ff, lora ? fi : nullptr, f, f, lp, lp, lp, lp, f, f,
+                          plan->ws_bytes, nullptr);
+      }
+    if (st != MOELORA_OK) break;
+  }
+  tl_resolve_only = false;
+  if (st == MOELORA_OK && bit) plan->resolved.fetch_or(bit, std::memory_order_acq_rel);
+  return st;
 }
 
 // Allocation-free calls: the workspace lives in a file-scope device array.

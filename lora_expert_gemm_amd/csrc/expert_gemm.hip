@@ -1050,8 +1050,7 @@ hipError_t launch_gu(const GemmArgs &a, int ntn, hipStream_t st) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(ntn * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(ntn * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
@@ -1086,8 +1085,7 @@ hipError_t launch_d(const GemmArgs &a, int ntn, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   const int ks = S > 0 ? a.ksplit : 1;
-  hipLaunchKernelGGL(kern, dim3(extra + ntn * ks * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(extra + ntn * ks * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2>
 hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
@@ -1120,15 +1118,13 @@ hipError_t go_down(const GemmArgs &a, hipStream_t st) {
 template <typename DT, int TG, bool VEC, bool EK, bool FROM_H>
 hipError_t go_shrink(const GemmArgs &a, hipStream_t st) {
   if (a.shrink_waves == 4)
-    hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H, 4>), dim3(a.s.max_tiles, a.split),
-                       dim3(4 * kWave), 0, st, a);
-  else if (a.shrink_waves == 8)
-    hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H, 8>), dim3(a.s.max_tiles, a.split),
-                       dim3(8 * kWave), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_shrink<DT, TG, VEC, EK, FROM_H, kShrinkWaves>),
+    return launch_kernel(k_shrink<DT, TG, VEC, EK, FROM_H, 4>, dim3(a.s.max_tiles, a.split),
+                         dim3(4 * kWave), 0, st, a);
+  if (a.shrink_waves == 8)
+    return launch_kernel(k_shrink<DT, TG, VEC, EK, FROM_H, 8>, dim3(a.s.max_tiles, a.split),
+                         dim3(8 * kWave), 0, st, a);
+  return launch_kernel(k_shrink<DT, TG, VEC, EK, FROM_H, kShrinkWaves>,
                        dim3(a.s.max_tiles, a.split), dim3(kShrinkWaves * kWave), 0, st, a);
-  return hipGetLastError();
 }
 
 // (vec, even_k) in {(1,1), (1,0), (0,0)}: unaligned rows always mask.
@@ -1194,36 +1190,37 @@ hipError_t launch_combine(const Shape &s, const int *ids, const float *w, const 
   if (s.T == 0) return hipSuccess;
   if (z_d) {
     const dim3 grid(s.T, (s.H + 63) / 64);
-#define MOELORA_COMB(DT, V, KB)                                                                \
-  hipLaunchKernelGGL((k_combine_rows<DT, V, KB>), grid, dim3(64), 0, st, s, ids, w, y, ksplit, \
-                     static_cast<DT *>(out), z_d, static_cast<const DT *>(B_d), adapter_ids)
+#define MOELORA_COMB(DT, V, KB)                                                                  \
+  return launch_kernel(k_combine_rows<DT, V, KB>, grid, dim3(64), 0, st, s, ids, w, y, ksplit, \
+                       static_cast<DT *>(out), z_d, static_cast<const DT *>(B_d), adapter_ids)
 #define MOELORA_COMB_K(DT, V)                                                                  \
   do {                                                                                         \
     if (s.k == 1) MOELORA_COMB(DT, V, 1);                                                      \
-    else if (s.k == 2) MOELORA_COMB(DT, V, 2);                                                 \
-    else MOELORA_COMB(DT, V, 4);                                                               \
+    if (s.k == 2) MOELORA_COMB(DT, V, 2);                                                      \
+    MOELORA_COMB(DT, V, 4);                                                                    \
   } while (0)
     if (bf16) {
-      if (vec) MOELORA_COMB_K(uint16_t, true); else MOELORA_COMB_K(uint16_t, false);
-    } else {
-      if (vec) MOELORA_COMB_K(float, true); else MOELORA_COMB_K(float, false);
+      if (vec) MOELORA_COMB_K(uint16_t, true);
+      MOELORA_COMB_K(uint16_t, false);
     }
+    if (vec) MOELORA_COMB_K(float, true);
+    MOELORA_COMB_K(float, false);
 #undef MOELORA_COMB_K
 #undef MOELORA_COMB
-    return hipGetLastError();
   }
   const dim3 grid(s.T, (s.H + 1023) / 1024);
-#define MOELORA_COMB(DT, V)                                                                    \
-  hipLaunchKernelGGL((k_combine<DT, V>), grid, dim3(256), 0, st, s, ids, w, y, ksplit,         \
-                     static_cast<DT *>(out), nullptr, nullptr, nullptr)
+#define MOELORA_COMB(DT, V)                                                                      \
+  return launch_kernel(k_combine<DT, V>, grid, dim3(256), 0, st, s, ids, w, y, ksplit,          \
+                       static_cast<DT *>(out), static_cast<const float *>(nullptr),             \
+                       static_cast<const DT *>(nullptr), static_cast<const int *>(nullptr))
   const bool v4 = s.H % 4 == 0;
   if (bf16) {
-    if (v4) MOELORA_COMB(uint16_t, true); else MOELORA_COMB(uint16_t, false);
-  } else {
-    if (v4) MOELORA_COMB(float, true); else MOELORA_COMB(float, false);
+    if (v4) MOELORA_COMB(uint16_t, true);
+    MOELORA_COMB(uint16_t, false);
   }
+  if (v4) MOELORA_COMB(float, true);
+  MOELORA_COMB(float, false);
 #undef MOELORA_COMB
-  return hipGetLastError();
 }
 
 }  // namespace moelora

@@ -9,6 +9,25 @@
 
 namespace moelora {
 
+// Kernel resolution.  The HIP runtime loads a source file's code object and
+// looks a kernel's symbol up on the first launch of that kernel on a device.
+// The first forward of a plan on a device therefore runs its dispatch once
+// for every kernel selection any token count of the plan can make, on this
+// thread only, with tl_resolve_only set: launch_kernel then looks the
+// kernel up (hipFuncGetAttributes) instead of launching it, and later
+// forwards load no code at any token count.
+extern thread_local bool tl_resolve_only;
+template <typename F, typename... Args>
+inline hipError_t launch_kernel(F kern, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                                Args... args) {
+  if (tl_resolve_only) {
+    hipFuncAttributes fa;
+    return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
+  }
+  hipLaunchKernelGGL(kern, grid, block, lds, st, args...);
+  return hipGetLastError();
+}
+
 // Shape of one forward call (token-count dependent parts included).
 struct Shape {
   int T, H, I, E, k, NA, r;

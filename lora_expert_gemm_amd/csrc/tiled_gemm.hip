@@ -590,8 +590,7 @@ hipError_t go_tiled(const GemmArgs &a, hipStream_t st) {
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(ntn * a.s.nblk), dim3(kTThreads), lds, st, a);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(ntn * a.s.nblk), dim3(kTThreads), lds, st, a);
 }
 
 template <bool GATE_UP, bool LORA>
@@ -602,8 +601,7 @@ hipError_t go_tiled8(const GemmArgs &a, hipStream_t st) {
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kT8Lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(kern, dim3(ntn * a.s.nblk), dim3(kT8Threads), kT8Lds, st, a);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(ntn * a.s.nblk), dim3(kT8Threads), kT8Lds, st, a);
 }
 
 template <bool GATE_UP, int BK>
@@ -620,14 +618,14 @@ hipError_t launch_tiled_shrink(const GemmArgs &a, bool from_h, hipStream_t st) {
   const int K = from_h ? a.s.I : a.s.H;
   const bool even = K % 64 == 0;
 #define MOELORA_TS(FH, EV) \
-  hipLaunchKernelGGL((k_tiled_shrink<FH, 64, EV>), dim3(a.s.max_tiles), dim3(kTThreads), 0, st, a)
+  return launch_kernel(k_tiled_shrink<FH, 64, EV>, dim3(a.s.max_tiles), dim3(kTThreads), 0, st, a)
   if (from_h) {
-    if (even) MOELORA_TS(true, true); else MOELORA_TS(true, false);
-  } else {
-    if (even) MOELORA_TS(false, true); else MOELORA_TS(false, false);
+    if (even) MOELORA_TS(true, true);
+    MOELORA_TS(true, false);
   }
+  if (even) MOELORA_TS(false, true);
+  MOELORA_TS(false, false);
 #undef MOELORA_TS
-  return hipGetLastError();
 }
 
 hipError_t launch_tiled(const GemmArgs &a, bool gate_up, const GemmVariant &v, hipStream_t st) {

@@ -7,7 +7,10 @@ summaries kept under ``profiles/``:
   (``<name>_kernel_stats.csv``);
 * ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (one counter per run):
   HBM bytes per dispatch, scaled by what the same counters report for a
-  plain device copy of known size (``<name>_counter_collection.csv``).
+  plain device copy of known size (``<name>_counter_collection.csv``);
+* ``--hip-trace --hsa-trace --memory-allocation-trace --kernel-trace`` of
+  ``tests/steady_state_child.py``: the HIP and HSA calls, allocations and
+  dispatches between the child's two marker calls (steady-state forwards).
 
 Kernels are keyed by the pipeline stage they implement, so a reader (such as
 bench.py's roofline) can find the bytes of "gate_up" whichever kernel
@@ -18,6 +21,7 @@ Usage::
     python -m lora_expert_gemm_amd.profiling stats <workload> <stats.csv> <out.md> <command...>
     python -m lora_expert_gemm_amd.profiling traffic <workload> <fetch.csv> <write.csv> \
         <copy_fetch.csv> <copy_write.csv> <copy_mib> <traffic.json> <out.md> <source_hash> <command...>
+    python -m lora_expert_gemm_amd.profiling steady <trace dir> <out.md> <command...>
 
 The trailing words are the rocprofv3 command(s) that made the CSVs, recorded
 in the summary; a ";;" word separates commands.
@@ -148,12 +152,95 @@ def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
     return entry
 
 
+# Calls that load code or allocate: none may fall between the markers.
+CODE_OR_MEMORY = ("hsa_executable_create", "hsa_executable_load", "hsa_executable_freeze",
+                  "hsa_code_object", "hsa_memory_allocate", "hsa_amd_memory_pool_allocate",
+                  "hsa_amd_memory_lock", "hipModule", "hipMalloc", "hipHostMalloc", "hipFree",
+                  "hipHostRegister", "__hipRegister")
+MARKER = "hipDriverGetVersion"
+
+
+def _csv(trace_dir, suffix):
+    for root, _, files in os.walk(trace_dir):
+        for f in files:
+            if f.endswith(suffix):
+                with open(os.path.join(root, f)) as fh:
+                    return list(csv.DictReader(fh))
+    return []
+
+
+def steady_window(trace_dir):
+    """Counts of HIP / HSA calls, allocations and dispatches before the first
+    marker call and between the two markers of the steady-state child."""
+    hip = _csv(trace_dir, "_hip_api_trace.csv")
+    hsa = _csv(trace_dir, "_hsa_api_trace.csv")
+    mem = _csv(trace_dir, "_memory_allocation_trace.csv")
+    ker = _csv(trace_dir, "_kernel_trace.csv")
+    marks = sorted(int(r["Start_Timestamp"]) for r in hip if r["Function"] == MARKER)
+    if len(marks) != 2:
+        raise ValueError(f"expected two {MARKER} markers, found {len(marks)}")
+    a, b = marks
+
+    def split(rows, key):
+        before, inside = defaultdict(int), defaultdict(int)
+        for r in rows:
+            t = int(r["Start_Timestamp"])
+            if t < a:
+                before[r[key]] += 1
+            elif t < b and r[key] != MARKER:
+                inside[r[key]] += 1
+        return dict(before), dict(inside)
+
+    out = {}
+    out["hip_before"], out["hip_inside"] = split(hip, "Function")
+    out["hsa_before"], out["hsa_inside"] = split(hsa, "Function")
+    out["alloc_before"], out["alloc_inside"] = split(mem, "Operation")
+    kb, ki = split(ker, "Kernel_Name")
+    out["kernels_before"] = {short_name(k): v for k, v in kb.items()}
+    out["kernels_inside"] = {short_name(k): v for k, v in ki.items()}
+    out["forbidden_inside"] = {k: v for d in (out["hip_inside"], out["hsa_inside"])
+                               for k, v in d.items() if k.startswith(CODE_OR_MEMORY)}
+    return out
+
+
+def write_steady_md(trace_dir, out_md, command):
+    w = steady_window(trace_dir)
+    lines = ["# Steady-state forwards: code loads, allocations and API calls", "",
+             "One plan of a 128-expert top-8 layer (H 2048, I 768, 32 adapters of rank 16, "
+             "bf16) serves forwards at 1, 3, 24, 40, 64, 100, 256, 300, 700, 1024 and 2048 "
+             "tokens (16-, 32- and 64-row streaming blocks, row- and tile-wise LoRA, 128-row "
+             "LDS-tiled blocks).  The first forward runs before the first marker call; the "
+             "other 21 forwards run between the two markers (`tests/steady_state_child.py`).",
+             "", "Command (run from /tmp with TMPDIR=/tmp):", "", "```", command, "```", ""]
+
+    def table(title, d):
+        lines.extend([f"**{title}**", "", "| call | count |", "|---|---|"])
+        for k, v in sorted(d.items(), key=lambda kv: -kv[1]):
+            lines.append(f"| {k} | {v} |")
+        if not d:
+            lines.append("| (none) | 0 |")
+        lines.append("")
+
+    table("Code-object loads and allocations between the markers", w["forbidden_inside"])
+    table("Memory allocations between the markers", w["alloc_inside"])
+    table("HIP API calls between the markers", w["hip_inside"])
+    table("HSA API calls between the markers", w["hsa_inside"])
+    loads = {k: v for k, v in w["hsa_before"].items()
+             if k.startswith(("hsa_executable_load", "hsa_code_object"))}
+    table("Code-object loads before the first marker (start-up and the first forward)", loads)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return w
+
+
 def main(argv):
     # command words; a ";;" word starts a new command line
     def cmd(words):
         return " ".join(words).replace(" ;; ", "\n")
     if argv[0] == "stats":
         write_stats_md(argv[1], argv[2], argv[3], cmd(argv[4:]))
+    elif argv[0] == "steady":
+        write_steady_md(argv[1], argv[2], cmd(argv[3:]))
     elif argv[0] == "traffic":
         (wl, fcsv, wcsv, cfcsv, cwcsv, mib, tj, md, h), rest = argv[1:10], argv[10:]
         write_traffic(wl, fcsv, wcsv, cfcsv, cwcsv, float(mib), tj, md, h, cmd(rest))
