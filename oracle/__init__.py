@@ -26,7 +26,7 @@ _SRC = os.path.join(_HERE, "moelora_ref.c")
 _LIB_DIR = os.path.join(_HERE, "_lib")
 _LIB = os.path.join(_LIB_DIR, "libmoelora_ref.so")
 
-F32, BF16 = 0, 1
+F32, BF16, BF16_FP8W = 0, 1, 2
 
 
 _CFLAGS = ["-O2", "-fopenmp", "-std=c11", "-fPIC", "-shared"]
@@ -56,8 +56,10 @@ def _bind(path):
     lib.ref_align.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, P, P]
     lib.ref_align.restype = i
     lib.ref_forward.argtypes = [i, i, i, i, i, i, i, i,
-                                P, P, P, P, P, P, P, P, P, P, P, i, P]
+                                P, P, P, P, P, P, P, P, P, P, P, i, P, P, P]
     lib.ref_forward.restype = i
+    lib.ref_fp8_e4m3.argtypes = [i]
+    lib.ref_fp8_e4m3.restype = ctypes.c_double
     lib.ref_set_threads.argtypes = [i]
     lib.ref_set_threads.restype = i
     return lib
@@ -131,14 +133,19 @@ def ref_align(ids, adapter_ids, E, NA, BM, _lib_override=None):
 
 def ref_forward(x, ids, w, adapter_ids, W_gu, W_d, A_gu=None, B_gu=None,
                 A_d=None, B_d=None, *, inter, rank=0, n_adapters=0,
-                dtype=F32, tokens=None, _lib_override=None):
+                dtype=F32, tokens=None, W_gu_scale=None, W_d_scale=None,
+                _lib_override=None):
     """The layer output (float64) for the selected tokens.
 
     Arrays of the storage dtype are float32 (dtype=F32) or uint16 bf16 bit
-    patterns (dtype=BF16).  ``tokens`` selects rows of the output (all when
-    None); the result has shape [len(tokens)][H].
+    patterns (dtype=BF16).  With dtype=BF16_FP8W, x and the LoRA arrays are
+    bf16 patterns and W_gu / W_d are uint8 E4M3 codes with float32 scales
+    W_gu_scale [E][2I] and W_d_scale [E][H], one per weight row.
+    ``tokens`` selects rows of the output (all when None); the result has
+    shape [len(tokens)][H].
     """
     st = np.float32 if dtype == F32 else np.uint16
+    wt = np.uint8 if dtype == BF16_FP8W else st
     x = _c(x, st)
     T, H = x.shape
     ids = _c(ids, np.int32)
@@ -146,17 +153,23 @@ def ref_forward(x, ids, w, adapter_ids, W_gu, W_d, A_gu=None, B_gu=None,
     E = W_gu.shape[0]
     w = _c(w, np.float64)
     aid = _c(adapter_ids, np.int32)
-    arrs = [_c(a, st) for a in (W_gu, W_d, A_gu, B_gu, A_d, B_d)]
+    arrs = [_c(W_gu, wt), _c(W_d, wt)] + [_c(a, st) for a in (A_gu, B_gu, A_d, B_d)]
+    sg, sd = _c(W_gu_scale, np.float32), _c(W_d_scale, np.float32)
     sel = None if tokens is None else _c(tokens, np.int32)
     n_sel = T if sel is None else len(sel)
     out = np.zeros((n_sel, H), np.float64)
     rc = (_lib_override or _load()).ref_forward(T, H, inter, E, k, n_adapters, rank, dtype,
                              _ptr(x), _ptr(ids), _ptr(w), _ptr(aid),
                              *[_ptr(a) for a in arrs], _ptr(sel), n_sel,
-                             _ptr(out))
+                             _ptr(out), _ptr(sg), _ptr(sd))
     if rc:
         raise ValueError(f"ref_forward failed ({rc})")
     return out
+
+
+def fp8_e4m3(code, _lib_override=None):
+    """Value of an OCP E4M3 code (0..255) as the oracle decodes it."""
+    return float((_lib_override or _load()).ref_fp8_e4m3(int(code)))
 
 
 def set_threads(n):
@@ -169,7 +182,7 @@ class Variant:
     """The oracle's API bound to another build of the C source (used by the
     test that plants mistakes in a copy of the oracle to show the pins catch
     them)."""
-    F32, BF16 = F32, BF16
+    F32, BF16, BF16_FP8W = F32, BF16, BF16_FP8W
 
     def __init__(self, so_path):
         self._l = _bind(so_path)
@@ -182,6 +195,9 @@ class Variant:
 
     def ref_forward(self, *a, **kw):
         return ref_forward(*a, _lib_override=self._l, **kw)
+
+    def fp8_e4m3(self, code):
+        return fp8_e4m3(code, _lib_override=self._l)
 
 
 def build_variant(src_text, so_path):

@@ -39,6 +39,14 @@
  * thread in the order written below), so the result does not depend on the
  * thread count.  ref_set_threads fixes the count (0: the OpenMP default).
  *
+ * Low-precision base weights (dtype REF_BF16_FP8W).  x, the LoRA weights and
+ * the output are bf16 as above; W_gu and W_d hold one byte per element, an
+ * OCP 8-bit floating-point E4M3 code, and every weight row carries a float32
+ * scale: the weight is scale[row] times the code's value.  The pages name an
+ * FP8 fused-MoE path (the aib.vote news item on SageMaker fused-MoE kernel
+ * optimizations, second item) without a quantisation scheme; one scale per
+ * output row is the reading taken here.
+ *
  * Storage (row-major, contraction dimension contiguous):
  *   x        [T][H]
  *   W_gu     [E][2I][H]     rows 0..I-1 gate, rows I..2I-1 up
@@ -58,7 +66,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { REF_F32 = 0, REF_BF16 = 1 };
+enum { REF_F32 = 0, REF_BF16 = 1, REF_BF16_FP8W = 2 };
 
 /* Element i of an input array of the given storage type, widened to double. */
 static inline double ld(const void *p, size_t i, int dtype)
@@ -72,6 +80,36 @@ static inline double ld(const void *p, size_t i, int dtype)
 }
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/*
+ * Value of an OCP 8-bit floating-point E4M3 code: sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals
+ * m/8 * 2^-6; the codes with every exponent and mantissa bit set are NaN;
+ * there are no infinities (the largest finite magnitude is 1.75 * 2^8 = 448).
+ */
+double ref_fp8_e4m3(int code)
+{
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Element i of row `row` (rows of length K) of a base-weight array: the
+ * layer dtype, or for REF_BF16_FP8W scale[row] times the value of its code
+ * (fp8[c] holds the 256 code values). */
+static inline double ldw(const void *W, const float *scale, const double *fp8, size_t row,
+                         size_t K, size_t i, int dtype)
+{
+    if (dtype == REF_BF16_FP8W)
+        return (double)scale[row] * fp8[((const uint8_t *)W)[row * K + i]];
+    return ld(W, row * K + i, dtype);
+}
 
 /*
  * Router: for each token, softmax over its E logits, keep the k experts with
@@ -281,7 +319,8 @@ static void ref_token(int t, int T, int H, int I, int E, int k, int NA, int r, i
                       int lora, const void *x, const int32_t *ids, const double *w,
                       const int32_t *adapter_ids, const void *W_gu, const void *W_d,
                       const void *A_gu, const void *B_gu, const void *A_d,
-                      const void *B_d, double *o, double *g, double *h, double *y,
+                      const void *B_d, const float *s_gu, const float *s_d,
+                      const double *fp8, double *o, double *g, double *h, double *y,
                       double *z)
 {
     size_t I2 = 2 * (size_t)I;
@@ -299,9 +338,10 @@ static void ref_token(int t, int T, int H, int I, int E, int k, int NA, int r, i
         /* gate_up: base, then shrink and expand */
         for (size_t n = 0; n < I2; ++n) {
             double acc = 0.0;
-            size_t wrow = ((size_t)e * I2 + n) * H;
+            size_t wrow = (size_t)e * I2 + n;
             for (int c = 0; c < H; ++c)
-                acc += ld(x, (size_t)t * H + c, dtype) * ld(W_gu, wrow + c, dtype);
+                acc += ld(x, (size_t)t * H + c, dtype) *
+                       ldw(W_gu, s_gu, fp8, wrow, (size_t)H, (size_t)c, dtype);
             g[n] = acc;
         }
         if (a >= 0) {
@@ -327,9 +367,9 @@ static void ref_token(int t, int T, int H, int I, int E, int k, int NA, int r, i
         /* down: base, then shrink and expand */
         for (int m = 0; m < H; ++m) {
             double acc = 0.0;
-            size_t wrow = ((size_t)e * H + m) * I;
+            size_t wrow = (size_t)e * H + m;
             for (int i = 0; i < I; ++i)
-                acc += h[i] * ld(W_d, wrow + i, dtype);
+                acc += h[i] * ldw(W_d, s_d, fp8, wrow, (size_t)I, (size_t)i, dtype);
             y[m] = acc;
         }
         if (a >= 0) {
@@ -375,10 +415,16 @@ int ref_forward(int T, int H, int I, int E, int k, int NA, int r, int dtype,
                 const int32_t *adapter_ids, const void *W_gu, const void *W_d,
                 const void *A_gu, const void *B_gu, const void *A_d,
                 const void *B_d, const int32_t *tokens, int n_sel,
-                double *out_sel)
+                double *out_sel, const float *W_gu_scale, const float *W_d_scale)
 {
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || NA < 0 || r < 0)
         return -1;
+    if (dtype < REF_F32 || dtype > REF_BF16_FP8W ||
+        (dtype == REF_BF16_FP8W && (!W_gu_scale || !W_d_scale)))
+        return -1;
+    double fp8[256];
+    for (int c = 0; c < 256; ++c)
+        fp8[c] = ref_fp8_e4m3(c);
     int lora = A_gu && B_gu && A_d && B_d && adapter_ids && NA > 0 && r > 0;
     int nsel = tokens ? n_sel : T;
     int fail = 0;
@@ -400,8 +446,8 @@ int ref_forward(int T, int H, int I, int E, int k, int NA, int r, int dtype,
             if (fail)
                 continue;
             ref_token(tokens ? tokens[s] : s, T, H, I, E, k, NA, r, dtype, lora, x, ids, w,
-                      adapter_ids, W_gu, W_d, A_gu, B_gu, A_d, B_d,
-                      out_sel + (size_t)s * H, g, h, y, z);
+                      adapter_ids, W_gu, W_d, A_gu, B_gu, A_d, B_d, W_gu_scale, W_d_scale,
+                      fp8, out_sel + (size_t)s * H, g, h, y, z);
         }
         free(g);
         free(h);

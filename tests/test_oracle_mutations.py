@@ -20,8 +20,14 @@ MUTATIONS = {
                         "acc += z[c] * ld(B_gu, pair * I2 * r + (size_t)c * I2 + n, dtype);"),
     "a_d_row_stride_H": ("size_t arow = (pair * r + c) * I;",
                          "size_t arow = (pair * r + c) * H;"),
-    "w_gu_transposed": ("acc += ld(x, (size_t)t * H + c, dtype) * ld(W_gu, wrow + c, dtype);",
-                        "acc += ld(x, (size_t)t * H + c, dtype) * ld(W_gu, (size_t)e * I2 * H + (size_t)c * I2 + n, dtype);"),
+    "w_gu_transposed": ("ldw(W_gu, s_gu, fp8, wrow, (size_t)H, (size_t)c, dtype)",
+                        "ldw(W_gu, s_gu, fp8, (size_t)e * H + c, I2, n, dtype)"),
+    "fp8_scale_of_wrong_row": ("return (double)scale[row] * fp8[",
+                               "return (double)scale[row ^ 1] * fp8["),
+    "fp8_exponent_bias_8": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                            "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "fp8_subnormals_as_normals": ("if (e == 0)\n        v = ldexp((double)m / 8.0, -6);",
+                                  "if (e == 0)\n        v = ldexp(1.0 + (double)m / 8.0, -7);"),
     "no_renormalise": ("w[(size_t)t * k + j] = prob[ids[(size_t)t * k + j]] / kept;",
                        "w[(size_t)t * k + j] = prob[ids[(size_t)t * k + j]];"),
     "ties_to_higher_index": ("(best < 0 || l[e] > l[best])", "(best < 0 || l[e] >= l[best])"),
@@ -44,6 +50,9 @@ PIN_CALLS = [
     (pins.test_grouped_equals_dense, dict(seed=1)),
     (pins.test_single_adapter_equals_merged_weights, {}),
     (pins.test_identical_experts_make_routing_irrelevant, {}),
+    (pins.test_fp8_e4m3_codes_match_the_format, {}),
+    (pins.test_fp8_weights_equal_bf16_dequantised_weights, {}),
+    (pins.test_fp8_weights_against_dense_float64, {}),
 ]
 
 

@@ -303,3 +303,83 @@ def test_thread_count_does_not_change_results():
     finally:
         oracle.set_threads(0)
     assert np.array_equal(one, many)
+
+
+# ------------------------------------------------ fp8 (E4M3) base weights
+
+
+def _torch_e4m3(codes):
+    """float64 values of E4M3 codes by torch's float8_e4m3fn (a library
+    implementation of the same OCP format)."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def test_fp8_e4m3_codes_match_the_format(oracle_lib):
+    """All 256 codes against torch's float8_e4m3fn, and points of the OCP
+    E4M3 definition worked out by hand (bias 7, 3 mantissa bits, subnormals
+    at exponent 0, S.1111.111 = NaN, no infinities)."""
+    ours = np.array([oracle_lib.fp8_e4m3(c) for c in range(256)])
+    lib = _torch_e4m3(np.arange(256))
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], lib[~nan])
+    hand = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2 ** -6,
+            0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xBC: -1.5, 0xFE: -448.0}
+    for c, v in hand.items():
+        assert oracle_lib.fp8_e4m3(c) == v, hex(c)
+    assert np.signbit(oracle_lib.fp8_e4m3(0x80)) and oracle_lib.fp8_e4m3(0x80) == 0.0
+
+
+def fp8_workload(T=7, H=16, I=12, E=3, k=2, NA=2, r=4, seed=9, pow2=False):
+    """A small layer with E4M3 base weights (codes over every finite value)
+    and one scale per weight row; x and the adapters in bf16."""
+    w, d = small_workload(T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, seed=seed)
+    rng = np.random.default_rng(seed)
+    out = {n: (synth.f32_to_bf16_bits(v) if n in ("x", "A_gu", "B_gu", "A_d", "B_d") else v)
+           for n, v in d.items()}
+    for n, rows in (("W_gu", 2 * I), ("W_d", H)):
+        codes = rng.integers(0, 256, size=d[n].shape).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x3F        # no NaN codes
+        scale = (2.0 ** rng.integers(-4, 4, size=(E, rows)) if pow2
+                 else rng.uniform(0.01, 0.1, size=(E, rows))).astype(np.float32)
+        out[n], out[n + "_scale"] = codes, scale
+    return w, out
+
+
+def run_fp8(o, d, w, ids, wts, **kw):
+    return o.ref_forward(d["x"], ids, wts, d["adapter_ids"], d["W_gu"], d["W_d"], d["A_gu"],
+                         d["B_gu"], d["A_d"], d["B_d"], inter=w.I, rank=w.r, n_adapters=w.NA,
+                         dtype=o.BF16_FP8W, W_gu_scale=d["W_gu_scale"],
+                         W_d_scale=d["W_d_scale"], **kw)
+
+
+def test_fp8_weights_equal_bf16_dequantised_weights(oracle_lib):
+    """With power-of-two scales every dequantised weight (a 4-bit significand
+    times a power of two) is a bf16 value, so the fp8 layer must equal, bit
+    for bit, the bf16 layer on those weights (dequantised here with torch)."""
+    w, d = fp8_workload(pow2=True)
+    ids, wts = oracle_lib.ref_route(d["logits"], w.k)
+    deq = dict(d)
+    for n in ("W_gu", "W_d"):
+        v = _torch_e4m3(d[n]) * d[n + "_scale"][..., None].astype(np.float64)
+        b = synth.f32_to_bf16_bits(v.astype(np.float32))
+        assert np.array_equal(synth.bf16_bits_to_f32(b).astype(np.float64), v)
+        deq[n] = b
+    bf = oracle_lib.ref_forward(deq["x"], ids, wts, d["adapter_ids"], deq["W_gu"], deq["W_d"],
+                                d["A_gu"], d["B_gu"], d["A_d"], d["B_d"], inter=w.I, rank=w.r,
+                                n_adapters=w.NA, dtype=oracle_lib.BF16)
+    assert np.array_equal(run_fp8(oracle_lib, d, w, ids, wts), bf)
+
+
+def test_fp8_weights_against_dense_float64(oracle_lib):
+    """Arbitrary per-row scales: the fp8 layer against every expert evaluated
+    densely in float64 on weights dequantised with torch (scale x value)."""
+    w, d = fp8_workload(seed=4)
+    ids, wts = oracle_lib.ref_route(d["logits"], w.k)
+    dd = {n: (synth.bf16_bits_to_f32(v) if n in ("x", "A_gu", "B_gu", "A_d", "B_d") else v)
+          for n, v in d.items()}
+    for n in ("W_gu", "W_d"):
+        dd[n] = _torch_e4m3(d[n]) * d[n + "_scale"][..., None].astype(np.float64)
+    np.testing.assert_allclose(run_fp8(oracle_lib, d, w, ids, wts),
+                               dense_numpy(dd, ids, wts, w.I), rtol=1e-11, atol=1e-12)
