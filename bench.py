@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="timed calls of the prefill leg (0: no prefill leg)")
     ap.add_argument("--prefill-warmup", type=int, default=5)
+    ap.add_argument("--fp8-steps", type=int, default=200,
+                    help="timed calls of the E4M3-weight decode leg (0: none)")
     return ap.parse_args()
 
 
@@ -114,6 +116,8 @@ def algorithmic(w, ids, aid, row_mode=False):
     row-wise LoRA, the base GEMM and the down shrink (the expand then runs in
     the combine)."""
     s = 2 if w.dtype == "bf16" else 4
+    sw = 1 if w.wdtype == "fp8" else s     # bytes of a base-weight element
+    sc = 4 if w.wdtype == "fp8" else 0     # bytes of a row scale
     T, H, I, k, r = w.T, w.H, w.I, w.k, w.r
     valid = (ids >= 0) & (ids < w.E)
     experts = np.unique(ids[valid])
@@ -122,18 +126,22 @@ def algorithmic(w, ids, aid, row_mode=False):
     pairs = np.unique(np.stack([tok_a[lora_rows], ids[lora_rows]], 1), axis=0) \
         if lora_rows.any() else np.zeros((0, 2))
     n_exp, n_pair, R, R_lora = len(experts), len(pairs), int(valid.sum()), int(lora_rows.sum())
-    layer_bytes = s * (n_exp * 3 * H * I + n_pair * r * (2 * H + 3 * I) + 2 * T * H)
+    layer_bytes = n_exp * (3 * H * I * sw + (2 * I + H) * sc) + \
+        s * (n_pair * r * (2 * H + 3 * I) + 2 * T * H)
     layer_flop = R * 6 * H * I + R_lora * 2 * r * (2 * H + 3 * I)
     # the dominant kernels: gate_up (base 2I x H per expert, expand 2I x r per
     # pair, x in, h out, z in) and down (H x I per expert, H x r per pair, h in,
     # y out)
-    gu_bytes = s * (n_exp * 2 * I * H + n_pair * 2 * I * r + T * H + R * I) + 4 * R_lora * r
+    gu_bytes = n_exp * 2 * I * (H * sw + sc) + s * (n_pair * 2 * I * r + T * H + R * I) + \
+        4 * R_lora * r
     gu_flop = R * 4 * H * I + R_lora * 4 * I * r
     if row_mode:  # A_d read, z_d written by the shrinks riding along
-        dn_bytes = s * (n_exp * H * I + n_pair * I * r + R * I) + 4 * R * H + 4 * R_lora * r
+        dn_bytes = n_exp * H * (I * sw + sc) + s * (n_pair * I * r + R * I) + 4 * R * H + \
+            4 * R_lora * r
         dn_flop = R * 2 * H * I + R_lora * 2 * I * r
     else:         # B_d read, z_d read by the expand
-        dn_bytes = s * (n_exp * H * I + n_pair * H * r + R * I) + 4 * R * H + 4 * R_lora * r
+        dn_bytes = n_exp * H * (I * sw + sc) + s * (n_pair * H * r + R * I) + 4 * R * H + \
+            4 * R_lora * r
         dn_flop = R * 2 * H * I + R_lora * 2 * H * r
     return dict(n_exp=n_exp, n_pair=n_pair, R=R, R_lora=R_lora, layer_bytes=layer_bytes,
                 layer_flop=layer_flop, gate_up_bytes=gu_bytes, gate_up_flop=gu_flop,
@@ -281,7 +289,7 @@ def measure(torch, L, w, steps, warmup, no_lora=False, graph_steps=None):
     of its dominant kernel."""
     log(f"[bench] generating {w}")
     d = synth.make_inputs(w)
-    dtype = L.BF16 if w.dtype == "bf16" else L.F32
+    dtype = L.BF16_FP8W if w.wdtype == "fp8" else L.BF16 if w.dtype == "bf16" else L.F32
     plan = L.Plan(w.T, w.H, w.I, w.E, w.k, w.NA, w.r, dtype)
     info = plan.info(w.T)
     log(f"[bench] plan: {info}")
@@ -290,7 +298,10 @@ def measure(torch, L, w, steps, warmup, no_lora=False, graph_steps=None):
         a = a.view(np.int16) if a.dtype == np.uint16 else a
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    t = {n: dev(v) for n, v in d.items() if v is not None}
+    t = {n: dev(v) for n, v in d.items() if v is not None and not n.endswith("_scale")}
+    if w.wdtype == "fp8":  # E4M3 codes and row scales in the ABI's one-buffer layout
+        for n in ("W_gu", "W_d"):
+            t[n] = dev(L.fp8_weight_buffer(d[n], d[n + "_scale"]))
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
     out = torch.empty((w.T, w.H), dtype=torch.int16 if w.dtype == "bf16" else torch.float32,
                       device="cuda")
@@ -433,6 +444,17 @@ def main():
             "plan": p["plan"]}
         log(f"[bench] prefill: {p['ms']:.4f} ms/step, gate_up {pr['achieved']:.0f} TFLOP/s "
             f"({pr['frac']:.3f} of peak), layer {p['layer']['mfma_frac']:.3f} of MFMA peak")
+    if args.workload == DEFAULT_WORKLOAD and args.fp8_steps > 0 and not args.no_lora:
+        # the same decode step with E4M3 base weights and row scales
+        fw = synth.workload("decode_fp8w")
+        f = measure(torch, L, fw, args.fp8_steps, args.warmup)
+        res["decode_fp8w"] = {
+            "config": config_of(fw), "weights": "E4M3 codes + float32 row scales",
+            "steps": args.fp8_steps, "ms_per_step": f["ms"], "tokens_per_s": fw.T / (f["ms"] / 1e3),
+            "roofline": f["roof"], "layer": f["layer"], "kernels": f["kernels"],
+            "stages_ms": f["stage"], "plan": f["plan"]}
+        log(f"[bench] decode_fp8w: {f['ms']:.4f} ms/step, {f['roof']['kernel']} "
+            f"{f['roof']['achieved']:.0f} GB/s ({f['roof']['frac']:.3f} of peak)")
     print(json.dumps(res), flush=True)
 
 

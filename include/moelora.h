@@ -81,7 +81,22 @@ typedef enum moelora_status {
                                       static scratch buffer                */
 } moelora_status;
 
-typedef enum moelora_dtype { MOELORA_F32 = 0, MOELORA_BF16 = 1 } moelora_dtype;
+/* Element types.  MOELORA_BF16_FP8W: x, out and the LoRA weights bf16; the
+ * base weights W_gu and W_d one byte per element, an OCP 8-bit floating-point
+ * E4M3 code, with one float32 scale per weight row: the weight is
+ * scale[row] times the code's value (the aib.vote news item on SageMaker
+ * fused-MoE kernel optimizations, second item, routes FP8 MoE layers to a
+ * fused path; it gives no quantisation scheme, and one scale per output row
+ * is the reading taken here).  Each of w_gate_up / w_down then points at the
+ * codes, [E][2I][H] / [E][H][I] bytes, followed at the next 256-byte
+ * boundary (byte offset round_up(E*2I*H, 256) / round_up(E*H*I, 256)) by the
+ * scales, float32 [E][2I] / [E][H].  Requires H and I multiples of 64 and r
+ * a multiple of 8. */
+typedef enum moelora_dtype {
+    MOELORA_F32 = 0,
+    MOELORA_BF16 = 1,
+    MOELORA_BF16_FP8W = 2
+} moelora_dtype;
 
 /* Bits of the device error word. */
 #define MOELORA_DEVERR_EXPERT_ID 1   /* an expert id outside [0, E)        */

@@ -39,7 +39,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 ERR_TOO_LARGE = -6
 STATIC_SCRATCH_BYTES = 64 << 20
-F32, BF16 = 0, 1
+F32, BF16, BF16_FP8W = 0, 1, 2
 DEVERR_EXPERT_ID, DEVERR_ADAPTER_ID = 1, 2
 FLAG_DETERMINISTIC, FLAG_DEBUG_CHECK_IDS = 1, 2
 N_STAGES = 6
@@ -87,6 +87,20 @@ _lib.moelora_timing_begin.restype = ctypes.c_int
 _lib.moelora_timing_end.argtypes = [_P, ctypes.POINTER(ctypes.c_double), _I32,
                                     ctypes.POINTER(_I32)]
 _lib.moelora_timing_end.restype = ctypes.c_int
+
+
+def fp8_weight_buffer(codes, scales):
+    """The weight-buffer layout of MOELORA_BF16_FP8W as a numpy uint8 array:
+    the E4M3 codes ([E][rows][K] bytes), zero bytes up to the next 256-byte
+    boundary, then the float32 row scales ([E][rows])."""
+    import numpy as np
+    c = np.ascontiguousarray(codes, np.uint8).reshape(-1)
+    sc = np.ascontiguousarray(scales, np.float32).reshape(-1).view(np.uint8)
+    off = (c.size + 255) // 256 * 256
+    out = np.zeros(off + sc.size, np.uint8)
+    out[:c.size] = c
+    out[off:] = sc
+    return out
 
 
 class MoeLoraError(RuntimeError):

@@ -58,7 +58,8 @@ def _run(cmd, src):
     p = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in p.stderr.splitlines()
                     if _NOISE not in l and "kernel-resource-usage" not in l
-                    and not l.startswith(("  ", " |")) and l.strip() not in ("|", ""))
+                    and not re.match(r"^\s*(\d+\s*)?\|", l) and not l.startswith("  ")
+                    and l.strip() != "")
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stderr}")
     if err.strip():

@@ -187,7 +187,7 @@ struct Layout {
 
 // The weight stream of a projection runs through the LDS ring (bf16, the
 // contraction a multiple of 64), where 4-wave workgroups can share tokens.
-bool ring_ok(const moelora_desc &d, int K) { return d.dtype == MOELORA_BF16 && K % 64 == 0; }
+bool ring_ok(const moelora_desc &d, int K) { return d.dtype != MOELORA_F32 && K % 64 == 0; }
 
 Layout make_layout(const moelora_desc &d, const Tuning &tu, int T) {
   const bool share = tu.tok_share;
@@ -233,7 +233,7 @@ Layout make_layout(const moelora_desc &d, const Tuning &tu, int T) {
     L.ksplit = choose_ksplit(d, tu, s, tg, L.waves_d, share_d, L.down_rows);
   }
   L.split = choose_split(tg, s.R);
-  const size_t es = d.dtype == MOELORA_BF16 ? 2 : 4;
+  const size_t es = d.dtype == MOELORA_F32 ? 4 : 2;
   const size_t NB = (size_t)s.E * (s.NA + 1);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -268,13 +268,26 @@ Layout make_layout(const moelora_desc &d, const Tuning &tu, int T) {
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
-size_t elem_bytes(const moelora_desc &d) { return d.dtype == MOELORA_BF16 ? 2 : 4; }
+// Bytes of an activation / output / LoRA element, and of a base-weight element.
+size_t elem_bytes(const moelora_desc &d) { return d.dtype == MOELORA_F32 ? 4 : 2; }
+size_t weight_bytes(const moelora_desc &d) {
+  return d.dtype == MOELORA_BF16_FP8W ? 1 : elem_bytes(d);
+}
+// E4M3 base weights: the row scales follow the codes at the next 256-byte
+// boundary of the weight buffer.
+size_t scale_offset(size_t codes) { return (codes + 255) / 256 * 256; }
 
 moelora_status check_desc(const moelora_desc *d) {
   if (!d) return MOELORA_ERR_INVALID_ARG;
   if (d->flags & ~(uint32_t)(MOELORA_FLAG_DETERMINISTIC | MOELORA_FLAG_DEBUG_CHECK_IDS))
     return MOELORA_ERR_UNSUPPORTED;
-  if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16) return MOELORA_ERR_UNSUPPORTED;
+  if (d->dtype != MOELORA_F32 && d->dtype != MOELORA_BF16 && d->dtype != MOELORA_BF16_FP8W)
+    return MOELORA_ERR_UNSUPPORTED;
+  // E4M3 weights stream through the LDS ring only: contractions in 64-wide
+  // slabs, 16-byte aligned adapter rows
+  if (d->dtype == MOELORA_BF16_FP8W &&
+      (d->hidden % 64 != 0 || d->inter % 64 != 0 || d->rank % 8 != 0))
+    return MOELORA_ERR_UNSUPPORTED;
   if (d->n_experts < 1 || d->n_experts > 1024) return MOELORA_ERR_UNSUPPORTED;
   if (d->n_adapters < 0 || d->n_adapters > 255) return MOELORA_ERR_UNSUPPORTED;
   if ((long long)d->n_experts * (d->n_adapters + 1) > 8448) return MOELORA_ERR_UNSUPPORTED;
@@ -290,7 +303,8 @@ moelora_status check_desc(const moelora_desc *d) {
 
 GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora, bool rowz = false) {
   GemmVariant v;
-  v.bf16 = d.dtype == MOELORA_BF16;
+  v.bf16 = d.dtype != MOELORA_F32;
+  v.w8 = d.dtype == MOELORA_BF16_FP8W;
   const int epc = v.bf16 ? 8 : 4;
   const int ks = v.bf16 ? 32 : 16;
   v.tg = tg;
@@ -326,7 +340,7 @@ Selection selection_of(const moelora_plan_s *p, const Layout &L) {
 }
 
 int k_tail(const moelora_desc &d, int K) {
-  const int ks = d.dtype == MOELORA_BF16 ? 32 : 16;
+  const int ks = d.dtype == MOELORA_F32 ? 16 : 32;
   return (ks - K % ks) % ks;
 }
 
@@ -466,7 +480,7 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
            "k_tail_d=%d waves_gu=%d waves_d=%d down_rows=%d down_ksplit=%d lora_mode=%s "
            "shrink_split=%d shrink_waves=%d tok_share_gu=%d tok_share_d=%d cap=%d workspace=%zu",
-           vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
+           vg.w8 ? "bf16_fp8w" : vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
            k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, tg == kTgTiled ? 0 : down_rows,
            ksplit, d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile",
            L.split, plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(L.s, L.split),
@@ -614,13 +628,16 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
   {
     GemmArgs a = g;
     a.W = w_gate_up;
+    if (vg.w8)
+      a.wscale = reinterpret_cast<const float *>(
+          static_cast<const char *>(w_gate_up) + scale_offset((size_t)d.n_experts * 2 * d.inter * d.hidden));
     a.B = lora_b_gu;
     a.z = z_gu;
     a.z2 = z2_gu;
     a.waves = waves_gu;
     // (staggered walks: not for one expert, whose blocks all stream the same
     // rows: the dense 64-token gate_up 82 -> 79 us without)
-    a.rotate = plan->rotate && d.n_experts > 1 && (size_t)d.hidden * elem_bytes(d) % 4096 == 0;
+    a.rotate = plan->rotate && d.n_experts > 1 && (size_t)d.hidden * weight_bytes(d) % 4096 == 0;
     // 16-row blocks' gate_up with shared tokens: a 4-slot ring (the decode
     // step: 143 -> 139 us; 32-row blocks lose a workgroup per CU to it and
     // slow down 6-20 %)
@@ -641,11 +658,14 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
   {
     GemmArgs a = g;
     a.W = w_down;
+    if (vd.w8)
+      a.wscale = reinterpret_cast<const float *>(
+          static_cast<const char *>(w_down) + scale_offset((size_t)d.n_experts * d.hidden * d.inter));
     a.B = lora_b_d;
     a.z = z_d;
     a.z2 = z2_d;
     a.waves = waves_d;
-    a.rotate = plan->rotate && d.n_experts > 1 && (size_t)d.inter * elem_bytes(d) % 4096 == 0;
+    a.rotate = plan->rotate && d.n_experts > 1 && (size_t)d.inter * weight_bytes(d) % 4096 == 0;
     if (row) {
       a.rs = RowShrinkArgs{h, lora_a_d, z_d, adapter_ids, d.inter, vd.vec};
       a.row_wgs = s.R;
@@ -653,7 +673,7 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
     MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, false, vd, st) : launch_down(a, vd, st));
   }
   MOELORA_TRY(mark());
-  MOELORA_TRY(launch_combine(s, ids, wts, g.y, g.ksplit, out, d.dtype == MOELORA_BF16,
+  MOELORA_TRY(launch_combine(s, ids, wts, g.y, g.ksplit, out, d.dtype != MOELORA_F32,
                              row ? z_d : nullptr,
                              lora_b_d, adapter_ids, vd.vec, st));
   MOELORA_TRY(mark());

@@ -11,6 +11,7 @@
 namespace moelora {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -144,5 +145,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
+
+// Eight OCP E4M3 codes (code i in byte i % 4 of w[i / 4]) as one MFMA
+// operand chunk of eight bf16 values.  Every E4M3 value is a bf16 value, so
+// the conversion (two codes per instruction, scale 1) is exact; an in-bounds
+// check of the instruction on all 256 codes, both halves of the source
+// dword, matched the format's definition.
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return u32x4_t{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+}
 
 }  // namespace moelora

@@ -286,6 +286,10 @@ __device__ __forceinline__ void dma16(const uint16_t *src, unsigned char *lds, b
   else
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
+__device__ __forceinline__ void dma16_bytes(const uint8_t *src, unsigned char *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0,
+                                   kCpolNonTemporal);
+}
 template <int NG, int NW, int S>
 __device__ __forceinline__ void contract_shared(const uint16_t *const *dsrc, const uint16_t *tbase,
                                                 size_t ld, const int *tok_row, int K, int kg,
@@ -371,12 +375,277 @@ __device__ __forceinline__ void contract_shared_groups(const uint16_t *const *ds
     contract_shared<1, NW, S>(dsrc, tbase, ld, tok_row, K, kg, ri, wave, rot, tring, tslot, wring,
                               acc0, acc1);
 }
+// E4M3 weight stream (contract_dma8 / contract_shared8: the two ring forms
+// above with one-byte base weights and one scale per weight row).  A slab
+// is 128 contraction elements, so a 16-row weight tile is again 16 rows x
+// 128 bytes (whole lines, the same two global_load_lds_dwordx4 per tile and
+// the same slot size and chunk swizzle); a contraction that is an odd
+// multiple of 64 ends with a 64-wide tail slab whose upper chunks are
+// fetched from the lower ones (a valid address; those bytes are not used).
+// Lane (ri, kg) reads chunks kg and 4 + kg of row ri (16 codes each) and
+// covers, at k-step h = 0..3, contraction indices [16 c + 8 (h & 1), +8)
+// with c = kg + 4 (h >> 1) -- four lanes groups x 8 = 32 indices per step,
+// all 128 over the slab; its tokens are loaded for the same indices.  The
+// codes become bf16 operands in registers (e4m3x8_to_bf16, exact); the row
+// scales are applied by the caller after the contraction.  Loads per step:
+// 2 NW weight DMAs + 4 NG token loads (register tokens) or 2 NW + NG
+// (shared tokens), with the wait arithmetic of the bf16 forms.
+
+// Slab index of step j for a walk starting at rot (no rotation with a tail).
+__device__ __forceinline__ int slab_of(int j, int rot, int nsl) {
+  return j + rot >= nsl ? j + rot - nsl : j + rot;
+}
+
+template <int NG, int NW, int S>
+__device__ __forceinline__ void contract_dma8(const uint8_t *const *wrow, int coff, int coff_tail,
+                                              const uint16_t *const *xr, int K, int kg, int ri,
+                                              int rot, unsigned char *ring, f32x4_t *acc0,
+                                              f32x4_t *acc1) {
+  using M = Mma<uint16_t>;
+  static_assert(S >= 2, "a slot is refilled while another is read");
+  constexpr int kSlot = NW * 2048;
+  constexpr int kPer = 2 * NW + 4 * NG;    // vector loads issued per step
+  static_assert(kPer < 64, "vmcnt immediate");
+  constexpr int kWait = waitcnt_vm(kPer);
+  const int nsl = (K + 127) / 128;
+  const bool tail = K % 128 != 0;           // the last slab holds 64 elements
+  if (tail) rot = 0;
+  auto dma = [&](int j, int p) {
+    j = slab_of(j, rot, nsl);
+    const int off = 128 * j + (tail && j == nsl - 1 ? coff_tail : coff);
+    unsigned char *d = ring + p * kSlot;
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(wrow[2 * t + i] + off,
+                                         (__attribute__((address_space(3))) void *)(d + t * 2048 + i * 1024),
+                                         16, 0, kCpolNonTemporal);
+  };
+  struct Tok {
+    u32x4_t b[4][NG];
+  };
+  auto tload = [&](Tok &tk, int j) {
+    j = slab_of(j, rot, nsl);
+    const bool tj = tail && j == nsl - 1;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int c = kg + (h >= 2 && !tj ? 4 : 0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) tk.b[h][g] = load_chunk(xr[g], 128 * j + 16 * c + 8 * (h & 1));
+    }
+  };
+  auto compute = [&](int p, const Tok &tk, bool last_tail) {
+    const unsigned char *d = ring + p * kSlot + ri * 128;
+    const int clo = (kg ^ (ri & 7)) << 4, chi = ((4 + kg) ^ (ri & 7)) << 4;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      f32x4_t *acc = t == 0 ? acc0 : acc1;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(d + t * 2048 + clo);
+      const u32x4_t a0 = e4m3x8_to_bf16(lo[0], lo[1]), a1 = e4m3x8_to_bf16(lo[2], lo[3]);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        M::step(acc[g], a0, tk.b[0][g]);
+        M::step(acc[g], a1, tk.b[1][g]);
+      }
+      if (!last_tail) {
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(d + t * 2048 + chi);
+        const u32x4_t a2 = e4m3x8_to_bf16(hi[0], hi[1]), a3 = e4m3x8_to_bf16(hi[2], hi[3]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          M::step(acc[g], a2, tk.b[2][g]);
+          M::step(acc[g], a3, tk.b[3][g]);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) dma(min(j, nsl - 1), j);
+  auto step = [&](int j, const Tok &tk, Tok &tn, bool last_tail) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // slot (j + S - 1) % S has been read out
+    asm volatile("" ::: "memory");
+    dma(min(j + S - 1, nsl - 1), (j + S - 1) % S);
+    tload(tn, min(j + 1, nsl - 1));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWait);
+    asm volatile("" ::: "memory");
+    compute(j % S, tk, last_tail);
+  };
+  Tok ta, tb;
+  tload(ta, 0);
+  // every step but the last one in pairs; the last step may be the tail
+  int j = 0;
+  for (; j + 2 <= nsl - 1; j += 2) {
+    step(j, ta, tb, false);
+    step(j + 1, tb, ta, false);
+  }
+  if (j < nsl - 1) {
+    step(j, ta, tb, false);
+    step(j + 1, tb, ta, tail);
+  } else {
+    step(j, ta, tb, tail);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load of the ring lands after the wave leaves it
+}
+
+template <int TG, int NW, int S>
+__device__ __forceinline__ void contract_dma8_groups(const uint8_t *const *wrow, int coff,
+                                                     int coff_tail, const uint16_t *const *xr,
+                                                     int ntg, int K, int kg, int ri, int rot,
+                                                     unsigned char *ring, f32x4_t *acc0,
+                                                     f32x4_t *acc1) {
+  if (TG >= 4 && ntg > 2)
+    contract_dma8<TG, NW, S>(wrow, coff, coff_tail, xr, K, kg, ri, rot, ring, acc0, acc1);
+  else if (TG >= 2 && ntg > 1)
+    contract_dma8<(TG >= 2 ? 2 : 1), NW, S>(wrow, coff, coff_tail, xr, K, kg, ri, rot, ring, acc0,
+                                            acc1);
+  else
+    contract_dma8<1, NW, S>(wrow, coff, coff_tail, xr, K, kg, ri, rot, ring, acc0, acc1);
+}
+
+// Shared-token form: each group's token slab (16 rows x 128 bf16 = 4 KB)
+// sits in LDS as two halves of 16 rows x 128 bytes (contraction [0, 64) and
+// [64, 128) of the slab), each written by two whole-line DMAs of 8 rows, so
+// a slab is 4 NG token loads dealt round the waves (NG per wave).
+template <int NG, int NW, int S>
+__device__ __forceinline__ void contract_shared8(const uint8_t *const *wrow, int coff, int coff_tail,
+                                                 const uint16_t *tbase, size_t ld,
+                                                 const int *tok_row, int K, int kg, int ri,
+                                                 int wave, int rot, unsigned char *tring,
+                                                 int tslot, unsigned char *wring, f32x4_t *acc0,
+                                                 f32x4_t *acc1) {
+  using M = Mma<uint16_t>;
+  constexpr int kTI = (4 * NG + kShareWaves - 1) / kShareWaves;  // token loads per wave
+  constexpr int kPer = 2 * NW + kTI;                              // loads per slab
+  constexpr int kYoung = (S - 2) * kPer;  // loads of the slabs issued after slab j
+  static_assert(S >= 2 && kYoung < 64, "vmcnt immediate");
+  constexpr int kWait = waitcnt_vm_lgkm0(kYoung);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nsl = (K + 127) / 128;
+  const bool tail = K % 128 != 0;
+  if (tail) rot = 0;
+  // token load q (0 <= q < 4 NG) of a slab: group q / 4, half (q / 2) % 2,
+  // rows 8 (q % 2) .. +7; lane l: row 8 (q % 2) + l / 8, source chunk
+  // (l % 8) ^ (l / 8) of the half
+  const uint16_t *tsrc[kTI];
+  int tq[kTI];
+#pragma unroll
+  for (int c = 0; c < kTI; ++c) {
+    const int q = (wave + c * kShareWaves) % (4 * NG);
+    const int row = 16 * (q / 4) + 8 * (q % 2) + (lane >> 3);
+    tq[c] = q;
+    tsrc[c] = tbase + (size_t)tok_row[row] * ld + 8 * ((lane & 7) ^ (lane >> 3));
+  }
+  auto issue = [&](int j, int p) {
+    j = slab_of(j, rot, nsl);
+    const bool tj = tail && j == nsl - 1;
+    const int off = 128 * j + (tj ? coff_tail : coff);
+    unsigned char *d = wring + p * NW * 2048;
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16_bytes(wrow[2 * t + i] + off, d + t * 2048 + i * 1024);
+    unsigned char *td = tring + p * tslot;
+#pragma unroll
+    for (int c = 0; c < kTI; ++c) {
+      const int q = tq[c], half = (q >> 1) & 1;
+      dma16(tsrc[c] + 128 * j + (tj ? 0 : 64 * half), td + (q >> 2) * 4096 + half * 2048 + (q & 1) * 1024,
+            false);
+    }
+  };
+  auto compute = [&](int p, bool last_tail) {
+    const unsigned char *d = wring + p * NW * 2048 + ri * 128;
+    const unsigned char *td = tring + p * tslot + ri * 128;
+    const int clo = (kg ^ (ri & 7)) << 4, chi = ((4 + kg) ^ (ri & 7)) << 4;
+    // token chunk of k-step h: element 16 c + 8 (h & 1), c = kg + 4 (h >> 1)
+    // -> half h >> 1, chunk 2 kg + (h & 1) of that half
+    const int t0 = ((2 * kg) ^ (ri & 7)) << 4, t1 = ((2 * kg + 1) ^ (ri & 7)) << 4;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      f32x4_t *acc = t == 0 ? acc0 : acc1;
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(d + t * 2048 + clo);
+      const u32x4_t a0 = e4m3x8_to_bf16(lo[0], lo[1]), a1 = e4m3x8_to_bf16(lo[2], lo[3]);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        M::step(acc[g], a0, *reinterpret_cast<const u32x4_t *>(td + g * 4096 + t0));
+        M::step(acc[g], a1, *reinterpret_cast<const u32x4_t *>(td + g * 4096 + t1));
+      }
+      if (!last_tail) {
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(d + t * 2048 + chi);
+        const u32x4_t a2 = e4m3x8_to_bf16(hi[0], hi[1]), a3 = e4m3x8_to_bf16(hi[2], hi[3]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          M::step(acc[g], a2, *reinterpret_cast<const u32x4_t *>(td + g * 4096 + 2048 + t0));
+          M::step(acc[g], a3, *reinterpret_cast<const u32x4_t *>(td + g * 4096 + 2048 + t1));
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) issue(min(j, nsl - 1), j);
+  for (int j = 0; j < nsl; ++j) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWait);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(j + S - 1, nsl - 1), (j + S - 1) % S);
+    compute(j % S, tail && j == nsl - 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load of the rings lands after the wave leaves them
+}
+
+template <int TG, int NW, int S>
+__device__ __forceinline__ void contract_shared8_groups(const uint8_t *const *wrow, int coff,
+                                                        int coff_tail, const uint16_t *tbase,
+                                                        size_t ld, const int *tok_row, int ntg,
+                                                        int K, int kg, int ri, int wave, int rot,
+                                                        unsigned char *tring, unsigned char *wring,
+                                                        f32x4_t *acc0, f32x4_t *acc1) {
+  constexpr int tslot = TG * 4096;
+  if (TG >= 4 && ntg > 2)
+    contract_shared8<TG, NW, S>(wrow, coff, coff_tail, tbase, ld, tok_row, K, kg, ri, wave, rot,
+                                tring, tslot, wring, acc0, acc1);
+  else if (TG >= 2 && ntg > 1)
+    contract_shared8<(TG >= 2 ? 2 : 1), NW, S>(wrow, coff, coff_tail, tbase, ld, tok_row, K, kg, ri,
+                                               wave, rot, tring, tslot, wring, acc0, acc1);
+  else
+    contract_shared8<1, NW, S>(wrow, coff, coff_tail, tbase, ld, tok_row, K, kg, ri, wave, rot,
+                               tring, tslot, wring, acc0, acc1);
+}
+
+// The E4M3 weight rows of one DMA lane: rows 8 i + lane / 8 of each 16-row
+// tile, and its chunk's byte offset within a slab (full and tail slab).
+struct W8Rows {
+  const uint8_t *row[4];
+  int coff, coff_tail;
+};
+
+// Scales of the four weight rows an MFMA output lane holds (rows
+// m + 4 kg .. +3 of a 16-row tile at m), applied to the accumulators.
+template <int TG>
+__device__ __forceinline__ void scale_rows(const float *scale, int kg, f32x4_t *acc) {
+  const float4 s4 = *reinterpret_cast<const float4 *>(scale + 4 * kg);
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    acc[tg][0] *= s4.x;
+    acc[tg][1] *= s4.y;
+    acc[tg][2] *= s4.z;
+    acc[tg][3] *= s4.w;
+  }
+}
+
 // Starting slab of a workgroup's weight walk (contract_dma): staggered over
 // column tiles when a.rotate is set, else 0.  Keyed on the column tile, not
 // the workgroup, so that the blocks of one expert, which stream the same
 // weight rows, walk them in step and can meet in L2.
 __device__ __forceinline__ int walk_start(const GemmArgs &a, int K, int col_tile) {
   return a.rotate ? (int)(((unsigned)col_tile * 7u) % (unsigned)(K / 64)) : 0;
+}
+// The same for the E4M3 stream's 128-wide slabs.
+__device__ __forceinline__ int walk_start8(const GemmArgs &a, int K, int col_tile) {
+  return a.rotate ? (int)(((unsigned)col_tile * 7u) % (unsigned)((K + 127) / 128)) : 0;
 }
 
 // z values of a lane's rows for the batched expand below: row mode, z of
@@ -562,7 +831,8 @@ __device__ __forceinline__ GemmTile gemm_tile(int nblk, int bid, int nb) {
 // 2 row-wise (z per routed row).  S > 0: weights streamed through an S-slot
 // LDS ring per wave (contract_dma); SH: with the block's tokens shared by
 // the workgroup's kShareWaves waves (contract_shared).
-template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, int S, bool SH = false>
+template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, int S, bool SH = false,
+          bool W8 = false>
 __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
@@ -609,32 +879,60 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   if constexpr (S > 0) {
     // DMA rows: tile 0 = gate rows n0 .., tile 1 = the matching up rows
     extern __shared__ __align__(16) unsigned char smem[];
-    const uint16_t *dsrc[4];  // [tile][instruction]
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * i + (lane >> 3);
-      const uint16_t *g = static_cast<const uint16_t *>(a.W) +
-                          ((size_t)e * 2 * I + min(n0 + r, I - 1)) * H + 8 * ((lane & 7) ^ (r & 7));
-      dsrc[i] = g;
-      dsrc[2 + i] = g + (size_t)I * H;
-    }
+    unsigned char *tring = smem;
+    int *tok_row = reinterpret_cast<int *>(smem + tok_row_offset(TG, S, W8));
     if constexpr (SH) {
-      int *tok_row = reinterpret_cast<int *>(smem);
       if (threadIdx.x < BM) {
         const int p = a.al.sorted_rows[blk * BM + threadIdx.x];
         tok_row[threadIdx.x] = (p < s.R ? p : a.al.sorted_rows[blk * BM]) / s.k;
       }
       __syncthreads();
-      unsigned char *tring = smem + kTokRowBytes;
-      contract_shared_groups<TG, 2, S>(dsrc, static_cast<const uint16_t *>(a.x), (size_t)H, tok_row,
-                                       active_groups<TG>(a, blk), H, kg, ri, wave,
-                                       walk_start(a, H, gt.nt), tring,
-                                       tring + S * TG * 2048 + wave * S * 4096, ag, au);
-      if (n0 >= I) return;
+    }
+    const int ntg = active_groups<TG>(a, blk);
+    if constexpr (W8) {
+      const uint8_t *w8[4];  // [tile][instruction]: rows 8 i + lane / 8
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint8_t *g = static_cast<const uint8_t *>(a.W) +
+                           ((size_t)e * 2 * I + min(n0 + 8 * i + (lane >> 3), I - 1)) * H;
+        w8[i] = g;
+        w8[2 + i] = g + (size_t)I * H;
+      }
+      const int c8 = (lane & 7) ^ (lane >> 3);
+      const int rot = walk_start8(a, H, gt.nt);
+      if constexpr (SH) {
+        contract_shared8_groups<TG, 2, S>(w8, 16 * c8, 16 * (c8 & 3), static_cast<const uint16_t *>(a.x),
+                                          (size_t)H, tok_row, ntg, H, kg, ri, wave, rot, tring,
+                                          tring + S * TG * 4096 + wave * S * 4096, ag, au);
+        if (n0 >= I) return;
+      } else {
+        contract_dma8_groups<TG, 2, S>(w8, 16 * c8, 16 * (c8 & 3),
+                                       reinterpret_cast<const uint16_t *const *>(xr), ntg, H, kg, ri,
+                                       rot, smem + wave * S * 4096, ag, au);
+      }
+      // the row scales multiply the base contraction only, before the expand
+      const float *sc = a.wscale + (size_t)e * 2 * I + n0;
+      scale_rows<TG>(sc, kg, ag);
+      scale_rows<TG>(sc + I, kg, au);
     } else {
-      contract_dma_groups<TG, 2, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                    active_groups<TG>(a, blk), H, kg, ri, walk_start(a, H, gt.nt),
-                                    smem + wave * S * 4096, ag, au);
+      const uint16_t *dsrc[4];  // [tile][instruction]
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const uint16_t *g = static_cast<const uint16_t *>(a.W) +
+                            ((size_t)e * 2 * I + min(n0 + r, I - 1)) * H + 8 * ((lane & 7) ^ (r & 7));
+        dsrc[i] = g;
+        dsrc[2 + i] = g + (size_t)I * H;
+      }
+      if constexpr (SH) {
+        contract_shared_groups<TG, 2, S>(dsrc, static_cast<const uint16_t *>(a.x), (size_t)H, tok_row,
+                                         ntg, H, kg, ri, wave, walk_start(a, H, gt.nt), tring,
+                                         tring + S * TG * 2048 + wave * S * 4096, ag, au);
+        if (n0 >= I) return;
+      } else {
+        contract_dma_groups<TG, 2, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr), ntg, H, kg,
+                                      ri, walk_start(a, H, gt.nt), smem + wave * S * 4096, ag, au);
+      }
     }
   } else {
     contract<DT, TG, U, VEC, EVEN_K, true>(wg, wu, xr, active_groups<TG>(a, blk), H, kg, ag, au);
@@ -673,7 +971,7 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
 // over workgroups: split q sums its slab range into y[q] (the expand goes to
 // split 0), and the combine adds the partials in split order.
 template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2, int S,
-          bool SH = false>
+          bool SH = false, bool W8 = false>
 __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
@@ -742,31 +1040,60 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   if constexpr (S > 0) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NW = R2 ? 2 : 1;
-    const uint16_t *dsrc[2 * NW];  // [tile][instruction]
-#pragma unroll
-    for (int t = 0; t < NW; ++t)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 16 * t + 8 * i + (lane >> 3);
-        dsrc[2 * t + i] = static_cast<const uint16_t *>(a.W) + ((size_t)e * H + min(m0 + r, H - 1)) * I +
-                          k0 + 8 * ((lane & 7) ^ (r & 7));
-      }
+    unsigned char *tring = smem;
+    int *tok_row = reinterpret_cast<int *>(smem + tok_row_offset(TG, S, W8));
     if constexpr (SH) {
-      int *tok_row = reinterpret_cast<int *>(smem);
       if (threadIdx.x < BM)
         tok_row[threadIdx.x] =
             blk * BM + (a.al.sorted_rows[blk * BM + threadIdx.x] < s.R ? (int)threadIdx.x : 0);
       __syncthreads();
-      unsigned char *tring = smem + kTokRowBytes;
-      contract_shared_groups<TG, NW, S>(dsrc, static_cast<const uint16_t *>(a.h) + k0, (size_t)I,
-                                        tok_row, active_groups<TG>(a, blk), kn, kg, ri, wave,
-                                        walk_start(a, kn, gt.nt), tring,
-                                        tring + S * TG * 2048 + wave * S * NW * 2048, acc, acc1);
-      if (m0 >= H) return;
+    }
+    const int ntg = active_groups<TG>(a, blk);
+    if constexpr (W8) {
+      const uint8_t *w8[2 * NW];  // [tile][instruction]: rows 16 t + 8 i + lane / 8
+#pragma unroll
+      for (int t = 0; t < NW; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          w8[2 * t + i] = static_cast<const uint8_t *>(a.W) +
+                          ((size_t)e * H + min(m0 + 16 * t + 8 * i + (lane >> 3), H - 1)) * I + k0;
+      const int c8 = (lane & 7) ^ (lane >> 3);
+      const int rot = walk_start8(a, kn, gt.nt);
+      if constexpr (SH) {
+        contract_shared8_groups<TG, NW, S>(w8, 16 * c8, 16 * (c8 & 3),
+                                           static_cast<const uint16_t *>(a.h) + k0, (size_t)I,
+                                           tok_row, ntg, kn, kg, ri, wave, rot, tring,
+                                           tring + S * TG * 4096 + wave * S * NW * 2048, acc, acc1);
+        if (m0 >= H) return;
+      } else {
+        contract_dma8_groups<TG, NW, S>(w8, 16 * c8, 16 * (c8 & 3),
+                                        reinterpret_cast<const uint16_t *const *>(xr), ntg, kn, kg, ri,
+                                        rot, smem + wave * S * NW * 2048, acc, acc1);
+      }
+      const float *sc = a.wscale + (size_t)e * H + m0;
+      scale_rows<TG>(sc, kg, acc);
+      if (R2) scale_rows<TG>(sc + 16, kg, acc1);
     } else {
-      contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr),
-                                     active_groups<TG>(a, blk), kn, kg, ri, walk_start(a, kn, gt.nt),
-                                     smem + wave * S * NW * 2048, acc, acc1);
+      const uint16_t *dsrc[2 * NW];  // [tile][instruction]
+#pragma unroll
+      for (int t = 0; t < NW; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = 16 * t + 8 * i + (lane >> 3);
+          dsrc[2 * t + i] = static_cast<const uint16_t *>(a.W) + ((size_t)e * H + min(m0 + r, H - 1)) * I +
+                            k0 + 8 * ((lane & 7) ^ (r & 7));
+        }
+      if constexpr (SH) {
+        contract_shared_groups<TG, NW, S>(dsrc, static_cast<const uint16_t *>(a.h) + k0, (size_t)I,
+                                          tok_row, ntg, kn, kg, ri, wave, walk_start(a, kn, gt.nt),
+                                          tring, tring + S * TG * 2048 + wave * S * NW * 2048, acc,
+                                          acc1);
+        if (m0 >= H) return;
+      } else {
+        contract_dma_groups<TG, NW, S>(dsrc, reinterpret_cast<const uint16_t *const *>(xr), ntg, kn,
+                                       kg, ri, walk_start(a, kn, gt.nt), smem + wave * S * NW * 2048,
+                                       acc, acc1);
+      }
     }
   } else {
     contract<DT, TG, U, VEC, EVEN_K, R2>(wd, wd1, xr, active_groups<TG>(a, blk), I, kg, acc, acc1);
@@ -1040,11 +1367,11 @@ template <int TG, bool GATE_UP> constexpr int unroll_for() {
   return TG == 1 && !GATE_UP ? 6 : TG <= 2 ? 4 : 2;
 }
 
-template <typename DT, int TG, bool VEC, bool EK, int MODE, int S, bool SH = false>
+template <typename DT, int TG, bool VEC, bool EK, int MODE, int S, bool SH = false, bool W8 = false>
 hipError_t launch_gu(const GemmArgs &a, int ntn, hipStream_t st) {
-  auto kern = k_gate_up<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE, S, SH>;
+  auto kern = k_gate_up<DT, TG, unroll_for<TG, true>(), VEC, EK, MODE, S, SH, W8>;
   // two 16-row tiles (gate, up) per wave, plus the shared token ring
-  const int lds = SH ? shared_lds_bytes(TG, 2, S) : S * 4096 * a.waves;
+  const int lds = SH ? shared_lds_bytes(TG, 2, S, W8) : S * 4096 * a.waves;
   if (S > 0) {
     const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1057,6 +1384,15 @@ hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
   const int cols = 16 * a.waves;
   const int ntn = (a.s.I + cols - 1) / cols;
   if constexpr (sizeof(DT) == 2 && VEC && EK) {
+    if (a.wscale) {  // E4M3 weights: through the LDS ring only, 3 or 4 slots
+      if (a.s.H % 64 != 0 || a.s.I % 16 != 0) return hipErrorInvalidValue;
+      const bool sh = a.tok_share && a.waves == kShareWaves;
+      if (a.slots == 4)
+        return sh ? launch_gu<DT, TG, VEC, EK, MODE, 4, true, true>(a, ntn, st)
+                  : launch_gu<DT, TG, VEC, EK, MODE, 4, false, true>(a, ntn, st);
+      return sh ? launch_gu<DT, TG, VEC, EK, MODE, 3, true, true>(a, ntn, st)
+                : launch_gu<DT, TG, VEC, EK, MODE, 3, false, true>(a, ntn, st);
+    }
     if (a.s.H % 64 == 0) {
       if (a.slots == 2)
         return a.tok_share && a.waves == kShareWaves
@@ -1072,13 +1408,15 @@ hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
                    : launch_gu<DT, TG, VEC, EK, MODE, 4>(a, ntn, st);
     }
   }
+  if (a.wscale) return hipErrorInvalidValue;
   return launch_gu<DT, TG, VEC, EK, MODE, 0>(a, ntn, st);
 }
-template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2, int S, bool SH = false>
+template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2, int S, bool SH = false,
+          bool W8 = false>
 hipError_t launch_d(const GemmArgs &a, int ntn, hipStream_t st) {
-  auto kern = k_down<DT, TG, unroll_for<TG, R2>(), VEC, EK, MODE, R2, S, SH>;
+  auto kern = k_down<DT, TG, unroll_for<TG, R2>(), VEC, EK, MODE, R2, S, SH, W8>;
   const int extra = MODE == 2 ? a.row_wgs : 0;
-  const int lds = SH ? shared_lds_bytes(TG, R2 ? 2 : 1, S) : S * (R2 ? 4096 : 2048) * a.waves;
+  const int lds = SH ? shared_lds_bytes(TG, R2 ? 2 : 1, S, W8) : S * (R2 ? 4096 : 2048) * a.waves;
   if (S > 0) {
     const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1090,6 +1428,15 @@ hipError_t launch_d(const GemmArgs &a, int ntn, hipStream_t st) {
 template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2>
 hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
   if constexpr (sizeof(DT) == 2 && VEC && EK) {
+    if (a.wscale) {  // E4M3 weights: through the LDS ring only, 3 or 4 slots, no split
+      if (a.s.I % 64 != 0 || a.s.H % 16 != 0 || a.ksplit != 1) return hipErrorInvalidValue;
+      const bool sh = a.tok_share && a.waves == kShareWaves;
+      if (a.slots == 4)
+        return sh ? launch_d<DT, TG, VEC, EK, MODE, R2, 4, true, true>(a, ntn, st)
+                  : launch_d<DT, TG, VEC, EK, MODE, R2, 4, false, true>(a, ntn, st);
+      return sh ? launch_d<DT, TG, VEC, EK, MODE, R2, 3, true, true>(a, ntn, st)
+                : launch_d<DT, TG, VEC, EK, MODE, R2, 3, false, true>(a, ntn, st);
+    }
     if (a.s.I % 64 == 0) {
       if (a.slots == 2)
         return a.tok_share && a.waves == kShareWaves
@@ -1105,6 +1452,7 @@ hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
                    : launch_d<DT, TG, VEC, EK, MODE, R2, 4>(a, ntn, st);
     }
   }
+  if (a.wscale) return hipErrorInvalidValue;
   return launch_d<DT, TG, VEC, EK, MODE, R2, 0>(a, ntn, st);
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE>

@@ -72,7 +72,8 @@ struct GemmArgs {
   Shape s;
   const int *topk_ids;     // [R]
   const void *x;           // [T][H]
-  const void *W;           // base weights of this projection
+  const void *W;           // base weights of this projection (E4M3 codes for w8 variants)
+  const float *wscale;     // w8: one float32 scale per weight row, [E][rows]
   const void *A;           // LoRA A of this projection (shrink kernels)
   const void *B;           // LoRA B of this projection (expand epilogue)
   const float *z;          // [split][cap][r] shrink partial sums read by the expand,
@@ -110,12 +111,21 @@ inline bool ring_slots_supported(int s) { return s == 0 || s == 2 || s == 3 || s
 
 // Workgroups of kShareWaves waves with an LDS ring fetch the block's tokens
 // once into a shared LDS ring (GemmArgs::tok_share).  Their dynamic LDS:
-// token rows table, token ring, the waves' weight rings (NW 16-row tiles
-// each).
+// the token ring (S slots of TG groups x 16 rows x 64 bf16, or x 128 bf16
+// for the E4M3 stream's wider slabs), then the waves' weight rings (S slots
+// of NW 16-row tiles of 2 KB each).  The block's token-row table (BM ints)
+// sits in the token ring's last slot: it is only read while the waves set
+// up their token addresses, before that slot is first filled (the first
+// step's wait and barrier order the two), and keeping it out of the
+// footprint lets a 4-slot workgroup of 16-row blocks (and a 3-slot one of
+// 32-row E4M3 blocks) fit twice into a CU's 160 KB.
 constexpr int kShareWaves = 4;
-constexpr int kTokRowBytes = 256;
-constexpr int shared_lds_bytes(int TG, int NW, int S) {
-  return kTokRowBytes + S * TG * 2048 + kShareWaves * S * NW * 2048;
+constexpr int shared_lds_bytes(int TG, int NW, int S, bool w8 = false) {
+  return S * TG * (w8 ? 4096 : 2048) + kShareWaves * S * NW * 2048;
+}
+// Byte offset of the token-row table (in the token ring's last slot).
+constexpr int tok_row_offset(int TG, int S, bool w8 = false) {
+  return (S - 1) * TG * (w8 ? 4096 : 2048);
 }
 
 // Shrink kernels: one workgroup per LoRA tile, of kShrinkWaves waves (or 4
@@ -142,6 +152,8 @@ struct GemmVariant {
   bool lora;     // expand epilogue on
   bool rowz;     // row mode: z indexed by routed row (gate_up) / down shrink
                  // riding along and expand moved to the combine (down)
+  bool w8;       // base weights as E4M3 codes with row scales (bf16 layer,
+                 // weight stream through the LDS ring only)
 };
 hipError_t launch_gate_up(const GemmArgs &a, const GemmVariant &v, hipStream_t st);
 // LDS-tiled MFMA GEMM for 128-row blocks (bf16, 16-byte aligned rows): the

@@ -12,7 +12,12 @@ seed = 1000 + workload index for the named workloads):
   tensor 2  x [T][H] ~ N(0, 1);
   tensors 3..8  W_gu ~ N(0, 1/H), W_d ~ N(0, 1/I), A_gu ~ N(0, 1/H),
             B_gu ~ N(0, 1/r), A_d ~ N(0, 1/H), B_d ~ N(0, 1/r).
-N(0, v) means variance v.  Weight tensors are drawn per leading index i (an
+N(0, v) means variance v.  Workloads with E4M3 base weights (wdtype "fp8")
+draw W_gu and W_d the same way in float32 and store each weight row as
+OCP 8-bit E4M3 codes with one float32 scale: scale = max|row| / 448 (the
+format's largest finite value; 1 for an all-zero row), codes = the row
+divided by its scale, rounded to the nearest E4M3 value (ties to even, by
+torch's float8_e4m3fn conversion).  Weight tensors are drawn per leading index i (an
 expert, or an adapter-expert pair) in chunks of 2**22 elements, chunk c from
 ``default_rng([seed, tensor, i, c])``, so generation can run on several
 threads and gives the same bytes on any host.  Normal draws are float32;
@@ -48,6 +53,7 @@ class Workload:
     seq_len: int = 0  # tokens per sequence for the "per_sequence" scheme
     bias_var: float = 0.0  # variance of a per-expert router bias (0 = none)
     seed: int = 0
+    wdtype: str = ""  # base weights: "" (the layer dtype) or "fp8" (E4M3 + row scales)
 
 
 WORKLOADS = [
@@ -66,6 +72,16 @@ WORKLOADS = [
     # shape (the post's Figure 1 MLP); not one of the five reference configs
     Workload("dense_bf16", T=64, H=4096, I=11008, E=1, k=1, NA=16, r=32,
              dtype="bf16", adapters="uniform_with_none", seed=1005),
+    # E4M3 base weights with row scales (the low-precision weights of the
+    # aib.vote news item on SageMaker fused-MoE kernel optimizations, second
+    # item) on the decode, illustrative and many-expert shapes
+    Workload("decode_fp8w", T=16, H=2880, I=2880, E=32, k=4, NA=8, r=32,
+             dtype="bf16", adapters="uniform", seed=1006, wdtype="fp8"),
+    Workload("illustrative_fp8w", T=64, H=4096, I=11008, E=8, k=2, NA=16,
+             r=32, dtype="bf16", adapters="uniform_with_none", seed=1007, wdtype="fp8"),
+    Workload("many_expert_fp8w", T=256, H=2048, I=768, E=128, k=8, NA=32,
+             r=16, dtype="bf16", adapters="zipf_with_none", bias_var=0.5,
+             seed=1008, wdtype="fp8"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -186,9 +202,44 @@ def _stacked(seed, tensor, lead, shape, var, store):
     return out.reshape(tuple(lead) + tuple(shape))
 
 
+def quantize_e4m3_rows(f):
+    """float32 [..., rows, K] -> (uint8 E4M3 codes, float32 scales [..., rows]),
+    one scale per row (max|row| / 448, 1 for an all-zero row)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(f, np.float32))
+    amax = t.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (t / scale.unsqueeze(-1)).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), scale.numpy().astype(np.float32)
+
+
+def _stacked_fp8(seed, tensor, lead, shape, var):
+    """The float32 draws of _stacked (the same streams), each weight row
+    quantised to E4M3 with its scale, one leading index at a time."""
+    n = int(np.prod(lead))
+    m = int(np.prod(shape))
+    codes = np.empty((n,) + tuple(shape), np.uint8)
+    scales = np.empty((n, shape[0]), np.float32)
+    std = np.float32(np.sqrt(var))
+    f = np.empty(m, np.float32)
+
+    def job(i, c):
+        lo, hi = c * _CHUNK, min(m, (c + 1) * _CHUNK)
+        np.random.default_rng([seed, tensor, i, c]).standard_normal(out=f[lo:hi], dtype=np.float32)
+        f[lo:hi] *= std
+
+    nchunk = (m + _CHUNK - 1) // _CHUNK
+    with ThreadPoolExecutor(_workers()) as ex:
+        for i in range(n):
+            list(ex.map(lambda c: job(i, c), range(nchunk)))
+            codes[i], scales[i] = quantize_e4m3_rows(f.reshape(shape))
+    return codes.reshape(tuple(lead) + tuple(shape)), scales.reshape(tuple(lead) + (shape[0],))
+
+
 def make_inputs(w: Workload, lora=True):
     """All inputs of one layer call as numpy arrays in storage form
-    (float32, or uint16 bf16 bits for bf16 workloads)."""
+    (float32, or uint16 bf16 bits for bf16 workloads; E4M3 base weights as
+    uint8 codes with float32 row scales W_gu_scale [E][2I], W_d_scale [E][H])."""
     T, H, I, E, NA, r = w.T, w.H, w.I, w.E, w.NA, w.r
     rng = np.random.default_rng([w.seed, 0])
     logits = rng.standard_normal((T, E), dtype=np.float32)
@@ -199,8 +250,12 @@ def make_inputs(w: Workload, lora=True):
     st = w.dtype
     x = _stacked(w.seed, 2, (), (T, H), 1.0, st)
     d = dict(logits=logits, adapter_ids=aid, x=x)
-    d["W_gu"] = _stacked(w.seed, 3, (E,), (2 * I, H), 1.0 / H, st)
-    d["W_d"] = _stacked(w.seed, 4, (E,), (H, I), 1.0 / I, st)
+    if w.wdtype == "fp8":
+        d["W_gu"], d["W_gu_scale"] = _stacked_fp8(w.seed, 3, (E,), (2 * I, H), 1.0 / H)
+        d["W_d"], d["W_d_scale"] = _stacked_fp8(w.seed, 4, (E,), (H, I), 1.0 / I)
+    else:
+        d["W_gu"] = _stacked(w.seed, 3, (E,), (2 * I, H), 1.0 / H, st)
+        d["W_d"] = _stacked(w.seed, 4, (E,), (H, I), 1.0 / I, st)
     if lora and NA > 0 and r > 0:
         d["A_gu"] = _stacked(w.seed, 5, (NA, E), (r, H), 1.0 / H, st)
         d["B_gu"] = _stacked(w.seed, 6, (NA, E), (2 * I, r), 1.0 / r, st)

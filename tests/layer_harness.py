@@ -34,11 +34,15 @@ class Run:
                  wts=None, max_tokens=None, adapter_ids="given"):
         L = lib()
         self.w, self.d = w, d
-        self.dtype = L.BF16 if w.dtype == "bf16" else L.F32
+        self.dtype = L.BF16_FP8W if w.wdtype == "fp8" else L.BF16 if w.dtype == "bf16" else L.F32
         self.plan = L.Plan(max_tokens or w.T, w.H, w.I, w.E, w.k, w.NA, w.r, self.dtype)
         self.ws = torch.empty(max(self.plan.workspace_bytes, 256), dtype=torch.uint8,
                               device="cuda")
-        self.t = {n: dev(v) for n, v in d.items() if v is not None and n != "logits"}
+        self.t = {n: dev(v) for n, v in d.items()
+                  if v is not None and n != "logits" and not n.endswith("_scale")}
+        if w.wdtype == "fp8":  # codes and row scales in one buffer, as the ABI lays them out
+            for n in ("W_gu", "W_d"):
+                self.t[n] = dev(L.fp8_weight_buffer(d[n], d[n + "_scale"]))
         self.t["logits"] = dev(d["logits"])
         if ids is not None:
             self.t["ids"] = dev(np.ascontiguousarray(ids, np.int32))
@@ -104,7 +108,8 @@ class Run:
 
 
 def oracle_out(w, d, ids, wts, tokens=None, lora=True, adapter_ids="given"):
-    dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+    dt = oracle.BF16_FP8W if w.wdtype == "fp8" else oracle.BF16 if w.dtype == "bf16" \
+        else oracle.F32
     use = lora and w.NA > 0 and w.r > 0 and d["A_gu"] is not None
     aid = d["adapter_ids"] if adapter_ids == "given" else None
     return oracle.ref_forward(
@@ -112,7 +117,8 @@ def oracle_out(w, d, ids, wts, tokens=None, lora=True, adapter_ids="given"):
         d["A_gu"] if use else None, d["B_gu"] if use else None,
         d["A_d"] if use else None, d["B_d"] if use else None,
         inter=w.I, rank=w.r if use else 0, n_adapters=w.NA if use else 0, dtype=dt,
-        tokens=None if tokens is None else np.asarray(tokens, np.int32))
+        tokens=None if tokens is None else np.asarray(tokens, np.int32),
+        W_gu_scale=d.get("W_gu_scale"), W_d_scale=d.get("W_d_scale"))
 
 
 def check_close(got, ref, dtype, what=""):

@@ -395,7 +395,8 @@ def coverage_tokens(w, ref_al):
 
 # Workloads whose oracle run over every token stays within seconds on the
 # test host's cores; the 6400-token prefill compares the coverage sample.
-FULL = {"tiny_fp32", "decode_bf16", "illustrative_bf16", "many_expert_bf16", "dense_bf16"}
+FULL = {"tiny_fp32", "decode_bf16", "illustrative_bf16", "many_expert_bf16", "dense_bf16",
+        "decode_fp8w", "illustrative_fp8w", "many_expert_fp8w"}
 
 
 @pytest.mark.parametrize("name", [w.name for w in synth.WORKLOADS])
@@ -425,3 +426,69 @@ def test_named_workload(name):
     mr, fr = check_close(full[tok], ref, w.dtype, name)
     say(f"[parity] {name}: max_rel={mr:.3e} fro_rel={fr:.3e} tokens={len(tok)} of {w.T}")
     assert run.device_error() == 0
+
+
+# E4M3 base weights with row scales: contractions that are multiples of 128
+# and odd multiples of 64 (a 64-wide tail slab), 16-, 32- and 64-row
+# streaming blocks, row- and tile-wise LoRA, two-tile down waves, 4 KB
+# weight rows (staggered walks), one expert, no adapters.
+FP8 = [
+    # T, H, I, E, k, NA, r, adapters
+    (16, 256, 192, 8, 2, 3, 16, "uniform_with_none"),    # 16-row blocks, row LoRA, H % 128 == 0, I tail
+    (37, 192, 320, 6, 3, 5, 16, "uniform_with_none"),    # both tails, 16/32-row
+    (30, 128, 128, 8, 2, 3, 32, "uniform_with_none"),    # 32-row blocks, row-wise LoRA
+    (200, 128, 192, 64, 2, 3, 16, "uniform_with_none"),  # 32-row blocks, tile-wise LoRA
+    (300, 256, 320, 4, 2, 3, 16, "uniform_with_none"),   # 64-row blocks (no LDS-tiled path for E4M3)
+    (24, 4096, 256, 4, 2, 2, 16, "uniform_with_none"),   # 4 KB gate_up rows: staggered walks
+    (24, 256, 384, 1, 1, 3, 16, "uniform_with_none"),    # dense: one expert, top-1
+    (20, 192, 128, 8, 2, 0, 0, "none"),                  # no adapters
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r,ad", FP8)
+def test_fp8_weights(T, H, I, E, k, NA, r, ad):
+    w = synth.Workload("fp8", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16", adapters=ad,
+                       seed=T * 5 + H + I, wdtype="fp8")
+    say(f"[parity] fp8 {w}")
+    d = synth.make_inputs(w)
+    run = Run(w, d).forward()
+    say(f"[parity] plan {run.plan.info(T)}")
+    assert run.plan.info(T).startswith("dtype=bf16_fp8w")
+    rid, rw = oracle.ref_route(d["logits"], k)
+    ids, _ = run.routing()
+    assert np.array_equal(ids, rid)
+    mr, fr = check_close(run.out_f32(), oracle_out(w, d, rid, rw), "bf16", "fp8")
+    say(f"[parity] max_rel={mr:.3e} fro_rel={fr:.3e}")
+
+
+FP8_PATHS = [
+    (16, 256, 320, 8, 2, 3, 16),    # 16-row blocks, tail in the down contraction
+    (24, 192, 256, 4, 2, 3, 16),    # 32-row blocks, tail in gate_up
+    (200, 128, 256, 16, 2, 3, 16),  # 32-row blocks, tile-wise LoRA
+    (160, 128, 192, 8, 2, 3, 16),   # 64-row blocks
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r", FP8_PATHS)
+def test_fp8_stream_forms_agree(T, H, I, E, k, NA, r, monkeypatch):
+    """The E4M3 stream with tokens shared through LDS or loaded per wave, and
+    with 3 or 4 ring slots, feeds the MFMAs the same operands in the same
+    order: bit-identical outputs, each within the oracle's tolerance."""
+    w = synth.Workload("fp8paths", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
+                       adapters="uniform_with_none", seed=T * 3 + I, wdtype="fp8")
+    d = synth.make_inputs(w)
+    rid, rw = oracle.ref_route(d["logits"], k)
+    ref = oracle_out(w, d, rid, rw)
+    monkeypatch.setenv("MOELORA_WAVES_GU", "4")
+    monkeypatch.setenv("MOELORA_WAVES_D", "4")
+    outs = {}
+    for sh in ("1", "0"):
+        for slots in ("3", "4"):
+            monkeypatch.setenv("MOELORA_TOKSHARE", sh)
+            monkeypatch.setenv("MOELORA_SLOTS", slots)
+            run = Run(w, d).forward()
+            say(f"[parity] fp8 tokshare={sh} slots={slots} {w}: plan {run.plan.info(T)}")
+            outs[sh, slots] = run.out.cpu().numpy().copy()
+            check_close(run.out_f32(), ref, "bf16", f"fp8 tokshare {sh} slots {slots}")
+    for key, o in outs.items():
+        assert np.array_equal(o, outs["1", "3"]), f"{key} differs from shared tokens, 3 slots"

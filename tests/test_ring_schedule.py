@@ -220,15 +220,30 @@ def _functions(text):
 
 
 def _loops(lines):
-    """Bodies of the innermost loops: header label to the branch back to it."""
-    for i, l in enumerate(lines):
-        m = re.match(r"^(\.LBB\w+):\s*;\s*=>This Inner Loop Header", l)
-        if not m:
+    """Bodies of the innermost loops, in execution order: the compiler marks
+    each loop's header block and every other block of the loop ("in Loop:
+    Header=..."); the body is the header block and the member blocks after
+    it, then the member blocks laid out before it (a latch placed ahead of
+    the header)."""
+    blocks = []   # (label, annotation, lines)
+    for l in lines:
+        m = re.match(r"^(\.LBB\w+):\s*(;.*)?$", l)
+        if m:
+            blocks.append((m.group(1), m.group(2) or "", []))
+        elif blocks:
+            blocks[-1][2].append(l)
+    for i, (label, note, _) in enumerate(blocks):
+        if "=>This Inner Loop Header" not in note:
             continue
-        for k in range(i + 1, len(lines)):
-            if re.match(r"^\s*s_cbranch\w*\s+" + re.escape(m.group(1)) + r"\s*$", lines[k]):
-                yield lines[i + 1:k + 1]
-                break
+        tag = "Header=" + label.lstrip(".")
+        member = lambda b: b[0] == label or re.search(re.escape(tag) + r"\b", b[1])
+        after = [b for b in blocks[i:] if member(b)]
+        before = [b for b in blocks[:i] if member(b)]
+        body = []
+        for b in after + before:
+            body.append(f"{b[0]}:")
+            body.extend(b[2])
+        yield body
 
 
 def _hand_waits(body):
@@ -250,22 +265,25 @@ ASM = os.path.join(BUILD, "expert_gemm-gfx950.s")
                     "(python lora_expert_gemm_amd/build.py)")
 def test_compiled_ring_loops_issue_what_their_waits_count():
     text = open(ASM).read()
-    seen = {2: 0, 3: 0, 4: 0}
+    seen = {2: 0, 3: 0, 4: 0, "w8": 0}
     for (name, kind), lines in _functions(text):
-        args = _template_args(name)
-        S, SH = args[-2], bool(args[-1])
+        args = _template_args(name)   # ..., [R2,] S, SH, W8
+        S, SH, W8 = args[-3], bool(args[-2]), bool(args[-1])
         if S == 0:
             assert not any(_hand_waits(b) for b in _loops(lines)), name
             continue
         TG = args[0]
-        R2 = kind == "k_down" and bool(args[-3])
+        R2 = kind == "k_down" and bool(args[-4])
         NW = 2 if kind == "k_gate_up" or R2 else 1
         ngs = {1, 2, TG} & {1, 2, 4}
         ngs = {g for g in ngs if g <= TG}
+        # token loads per slab: 2 NG (bf16, 64-wide slabs) or 4 NG (E4M3,
+        # 128-wide slabs), dealt round the four waves when shared
+        tok = {g: (4 if W8 else 2) * g for g in ngs}
         if SH:
-            per = {2 * NW + (2 * g + SHARE_WAVES - 1) // SHARE_WAVES for g in ngs}
+            per = {2 * NW + (tok[g] + SHARE_WAVES - 1) // SHARE_WAVES for g in ngs}
         else:
-            per = {2 * NW + 2 * g for g in ngs}
+            per = {2 * NW + tok[g] for g in ngs}
         found = set()
         for body in _loops(lines):
             waits = _hand_waits(body)
@@ -286,6 +304,7 @@ def test_compiled_ring_loops_issue_what_their_waits_count():
             found.add(p)
         assert found, f"{name}: no ring loop with hand-written waits found"
         seen[S] += 1
+        seen["w8"] += W8
     assert all(seen.values()), seen
 
 
