@@ -666,6 +666,11 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
     a.z2 = z2_d;
     a.waves = waves_d;
     a.rotate = plan->rotate && d.n_experts > 1 && (size_t)d.inter * weight_bytes(d) % 4096 == 0;
+    // E4M3 weights, 16-row blocks with shared tokens: a 4-slot down ring too
+    // (the decode step's down 56 -> 53 us; bf16 unchanged by it, 32-row
+    // blocks slower)
+    if (vd.w8 && tg == kTgSmall && !plan->slots_forced && shares(plan, tg, waves_d, d.inter))
+      a.slots = 4;
     if (row) {
       a.rs = RowShrinkArgs{h, lora_a_d, z_d, adapter_ids, d.inter, vd.vec};
       a.row_wgs = s.R;
