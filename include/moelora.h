@@ -20,6 +20,8 @@
  * The router, when used, keeps the k largest logits (ties to the lower
  * expert index, listed largest first) and sets w = softmax over the kept
  * logits (softmax over all E followed by renormalisation over the kept k).
+ * Logits are expected to be finite: a NaN's place in the order is
+ * unspecified (the picks are still k distinct experts in range).
  * The post fixes neither the router formula, the activation nor the gate/up
  * split; these are the readings used here.
  *

@@ -32,16 +32,39 @@ __device__ __forceinline__ unsigned long long lanemask_lt(int lane) {
   return (1ull << lane) - 1ull;
 }
 
+// DPP controls (gfx9): quad permutations, row shifts, half-row and row
+// mirrors, broadcasts of a row's last lane into the rows above
+constexpr int kDppQuadSwap1 = 0xb1;  // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4e;  // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppRowShr = 0x110;  // + shift (1..15)
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+__device__ __forceinline__ unsigned dpp_max(unsigned x, unsigned y) { return x > y ? x : y; }
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_mov(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active), by
+// DPP: shifts by 1, 2, 4, 8 inside each 16-lane row (lanes shifted in from
+// outside the row read 0), then row 15's total added into rows 1 and 3 and
+// lane 31's into rows 2 and 3 -- six moves where lane shuffles pay an
+// LDS-crossbar round trip per step.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 1, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 2, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 4, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 8, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppBcast15, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppBcast31, 0xc, 0xf, false);
+  return x;
+}
+
 // Exclusive prefix sum over the 1024 threads of the block; *total gets the
 // sum.  tmp holds kAlignWaves ints.  Contains two barriers.
 __device__ int block_excl_scan(int v, int *tmp, int *total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == kWave - 1) tmp[w] = x;
   __syncthreads();
   int off = 0, tot = 0;
@@ -59,15 +82,7 @@ __device__ int block_excl_scan(int v, int *tmp, int *total) {
 // block_excl_scan of two values at once (same two barriers).
 __device__ int2 block_excl_scan2(int v0, int v1, int2 *tmp, int2 *total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int x0 = v0, x1 = v1;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y0 = __shfl_up(x0, d), y1 = __shfl_up(x1, d);
-    if (lane >= d) {
-      x0 += y0;
-      x1 += y1;
-    }
-  }
+  const int x0 = wave_incl_scan(v0), x1 = wave_incl_scan(v1);
   if (lane == kWave - 1) tmp[w] = make_int2(x0, x1);
   __syncthreads();
   int2 off = make_int2(0, 0), tot = make_int2(0, 0);
@@ -88,45 +103,66 @@ __device__ int2 block_excl_scan2(int v0, int v1, int2 *tmp, int2 *total) {
 
 // Router for one token, computed by one wave: the k largest logits (ties to
 // the lower expert index, largest first) and their softmax over the kept
-// logits.  Lane l holds experts l, l + 64, ...; each of the k rounds takes
-// the wave-wide best untaken (value, index) by a butterfly reduction.  Lanes
-// j < k end with the j-th pick in (*id, *wt).
+// logits.  Lane l holds experts l, l + 64, ...; each of the k rounds finds
+// the largest untaken logit and then, by ballots in expert order, the lowest
+// expert index holding it.  The maximum is taken on order-preserving
+// unsigned images of the floats (sign bit flipped for non-negative values,
+// every bit for negative ones; -0 taken as +0, which compares equal to it,
+// and every image at least 1, so 0 marks an absent or taken expert): DPP moves inside each 16-lane row (quad
+// swaps, then the half-row and row mirrors), then the four row maxima read
+// into scalars -- a few cycles per step where a butterfly of lane shuffles
+// pays an LDS-crossbar round trip per step.  Lanes j < k end with the j-th
+// pick in (*id, *wt).
 // SLOTS = experts per lane (E <= 64 * SLOTS), a template so that small
 // expert counts run a short serial path.
+__device__ __forceinline__ unsigned float_order_key(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;  // -0 -> +0
+  const unsigned key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return key > 1u ? key : 1u;  // only a negative NaN's image could be 0
+}
+__device__ __forceinline__ float float_of_order_key(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// the wave-wide maximum, in every lane (scalar)
+__device__ __forceinline__ unsigned wave_max_u32(unsigned x) {
+  x = dpp_max(x, dpp_mov<kDppQuadSwap1>(x));
+  x = dpp_max(x, dpp_mov<kDppQuadSwap2>(x));
+  x = dpp_max(x, dpp_mov<kDppHalfMirror>(x));  // lane i meets 7 - i: max of 8
+  x = dpp_max(x, dpp_mov<kDppMirror>(x));      // lane i meets 15 - i: max of 16
+  const unsigned r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const unsigned r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  return dpp_max(dpp_max(r0, r1), dpp_max(r2, r3));
+}
+
 template <int SLOTS>
 __device__ void route_token_rounds(const float *__restrict__ row, int E, int k, int *id, float *wt) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int per = SLOTS;
-  float v[SLOTS];
+  unsigned key[SLOTS];  // 0 for an absent or taken expert (below every logit's image)
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
     const int e = lane + i * kWave;
-    v[i] = e < E ? row[e] : -__builtin_inff();
+    key[i] = e < E ? float_order_key(row[e]) : 0u;
   }
-  unsigned taken = 0;  // bit i: expert lane + 64 i already chosen
   float my_val = 0.f, top = 0.f;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
+    unsigned m = 0;
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      const int e = lane + i * kWave;
-      if (i < per && e < E && !(taken >> i & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
+    for (int i = 0; i < SLOTS; ++i) m = dpp_max(m, key[i]);
+    m = wave_max_u32(m);
+    int bi = 0;
 #pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d);
-      const int oi = __shfl_xor(bi, d);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
+    for (int i = SLOTS - 1; i >= 0; --i) {  // the lowest slot holding m wins
+      const unsigned long long b = __ballot(key[i] == m);
+      if (b) bi = i * kWave + __ffsll((long long)b) - 1;
     }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if ((bi & (kWave - 1)) == lane) {
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i)
+        if (i == bi / kWave) key[i] = 0u;
+    }
+    const float bv = float_of_order_key(m);
     if (j == 0) top = bv;
     if (lane == j) {
       my_val = bv;
@@ -224,6 +260,17 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
   }
 }
 
+// The block size BM is a power of two (16, 32, 64 or 128 rows), so block
+// indices of positions are shifts: a division by a runtime value costs ~35
+// VALU instructions, and the plan and store loops below take one per bucket
+// and per (block, adapter), over thousands of buckets (in the 128-expert,
+// 32-adapter layer they were 14 of the one-workgroup kernel's 21 us).
+__device__ __forceinline__ int log2_bm(int BM) { return 31 - __builtin_clz(BM); }
+// blocks covered by the c >= 1 positions starting at st
+__device__ __forceinline__ int blocks_spanned(int st, int c, int lb) {
+  return ((st + c - 1) >> lb) - (st >> lb) + 1;
+}
+
 __device__ __forceinline__ int adapter_rank(const int *aid, int t, int NA, int &err) {
   if (!aid) return NA;
   const int a = aid[t];
@@ -298,7 +345,8 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
     pstart = hist[tid * NR];
     rows = (tid + 1 < E ? hist[(tid + 1) * NR] : total) - pstart;
   }
-  const int padded = (rows + BM - 1) / BM * BM;
+  const int lb = log2_bm(BM);
+  const int padded = ((rows + BM - 1) >> lb) << lb;
   int np;
   const int seg0 = block_excl_scan(padded, sm.scan_tmp, &np);
   if (owner) {
@@ -321,7 +369,7 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
         hist[b] = st;
         if (a < NA && P.c[i] > 0) {
           ++nseg;
-          ntile += (st + P.c[i] - 1) / BM - st / BM + 1;
+          ntile += blocks_spanned(st, P.c[i], lb);
         }
       }
       if (++a == NR) {
@@ -341,7 +389,7 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
       if (i < P.nb) {
         const int b = P.b0 + i;
         if (a == 0) sm.tile0[e] = ti;
-        if (a < NA && P.c[i] > 0) ti += (hist[b] + P.c[i] - 1) / BM - hist[b] / BM + 1;
+        if (a < NA && P.c[i] > 0) ti += blocks_spanned(hist[b], P.c[i], lb);
       }
       if (++a == NR) {
         a = 0;
@@ -360,14 +408,8 @@ __device__ AlignPlan align_plan(const Shape &s, AlignSmem &sm) {
 
 // Exclusive prefix sum over the 64 lanes of a wave; *total gets the sum.
 __device__ __forceinline__ int wave_excl_scan(int v, int *total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  *total = __shfl(x, kWave - 1);
+  const int x = wave_incl_scan(v);
+  *total = __builtin_amdgcn_readlane(x, kWave - 1);
   return x - v;
 }
 
@@ -408,7 +450,8 @@ __device__ AlignPlan align_plan_wave(const Shape &s, AlignSmem &sm) {
       pstart = hist[tid * NR];
       rows = (tid + 1 < E ? hist[(tid + 1) * NR] : total) - pstart;
     }
-    const int padded = (rows + BM - 1) / BM * BM;
+    const int lb = log2_bm(BM);
+    const int padded = ((rows + BM - 1) >> lb) << lb;
     int np;
     const int seg0 = wave_excl_scan(padded, &np);
     if (tid < E) {
@@ -429,7 +472,7 @@ __device__ AlignPlan align_plan_wave(const Shape &s, AlignSmem &sm) {
           hist[b] = st;
           if (a < NA && P.c[i] > 0) {
             ++nseg;
-            ntile += (st + P.c[i] - 1) / BM - st / BM + 1;
+            ntile += blocks_spanned(st, P.c[i], lb);
           }
         }
         if (++a == NR) {
@@ -449,7 +492,7 @@ __device__ AlignPlan align_plan_wave(const Shape &s, AlignSmem &sm) {
         if (i < P.nb) {
           const int b = P.b0 + i;
           if (a == 0) sm.tile0[e] = ti;
-          if (a < NA && P.c[i] > 0) ti += (hist[b] + P.c[i] - 1) / BM - hist[b] / BM + 1;
+          if (a < NA && P.c[i] > 0) ti += blocks_spanned(hist[b], P.c[i], lb);
         }
         if (++a == NR) {
           a = 0;
@@ -476,6 +519,7 @@ __device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan
   const int E = s.E, NA = s.NA, NR = NA + 1, BM = s.BM, R = s.R;
   const int *start = sm.hist;
   const int np = P.num_padded;
+  const int lb = log2_bm(BM);
   // the thread's buckets: start and row count, LoRA segment and block tiles
   int si = P.seg_off, ti = P.tile_off;
   int be = P.b0 / NR, ba = P.b0 - be * NR;  // (expert, rank) of bucket b0 + i
@@ -488,9 +532,10 @@ __device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan
       al.bucket_cnt[b] = c;
       if (ba < NA && c > 0) {
         reinterpret_cast<int4 *>(al.lora_seg)[si++] = make_int4(be, ba, st, c);
-        for (int blk = st / BM; blk <= (st + c - 1) / BM; ++blk) {
-          const int lo = max(st, blk * BM), hi = min(st + c, (blk + 1) * BM);
-          reinterpret_cast<int4 *>(al.tiles)[ti++] = make_int4(blk, ba, lo - blk * BM, hi - lo);
+        for (int blk = st >> lb; blk <= (st + c - 1) >> lb; ++blk) {
+          const int lo = max(st, blk << lb), hi = min(st + c, (blk + 1) << lb);
+          if (lo == blk << lb) al.block_tile_start[blk] = ti;  // the block's first tile
+          reinterpret_cast<int4 *>(al.tiles)[ti++] = make_int4(blk, ba, lo - (blk << lb), hi - lo);
         }
       }
     }
@@ -500,33 +545,35 @@ __device__ void align_store(const Shape &s, const AlignSmem &sm, const AlignPlan
     }
   }
   // blocks: expert (the last one whose segment starts at or before the
-  // block; empty experts share their start with the next) and first tile
-  // (the expert's first tile plus its tiles in earlier blocks)
+  // block; empty experts share their start with the next) and first tile.
+  // An expert's rows with an adapter come first, so a block has LoRA tiles
+  // exactly when its first position holds such a row, and then its first
+  // tile starts at the block start (written with the tiles above); any
+  // other block of expert e comes after all of e's tiles: its first tile is
+  // the next expert's first tile.
   for (int b = tid; b < s.nblk; b += kAlignThreads) {
     int e = -1, t = P.n_tiles;
-    if (b < np / BM) {
-      const int pos = b * BM;
+    bool tiled = false;
+    if (b < (np >> lb)) {
+      const int pos = b << lb;
       int lo = 0, hi = E;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (sm.seg0[mid] <= pos) lo = mid; else hi = mid;
       }
       e = lo;
-      t = sm.tile0[e];
-      for (int a = 0; a < NA; ++a) {
-        const int st = start[e * NR + a], c = start[e * NR + a + 1] - st;
-        if (c > 0) t += max(0, min(b, (st + c - 1) / BM + 1) - st / BM);
-      }
+      tiled = pos < start[e * NR + NA];  // the start of e's rows without an adapter
+      if (!tiled && e + 1 < E) t = sm.tile0[e + 1];
     }
     al.block_expert[b] = e;
-    al.block_tile_start[b] = t;
+    if (!tiled) al.block_tile_start[b] = t;
   }
   if (tid < E) al.seg_start[tid] = sm.seg0[tid];
   // padding sentinels: slot j < BM - 1 past the end of each expert's rows
-  for (int i = tid; i < E * (BM - 1); i += kAlignThreads) {
-    const int e = i / (BM - 1), j = i - e * (BM - 1);
+  for (int i = tid; i < (E << lb); i += kAlignThreads) {
+    const int e = i >> lb, j = i & (BM - 1);
     const int pos = sm.seg0[e] + sm.rows[e] + j;
-    if (pos < sm.seg0[e + 1]) al.sorted_rows[pos] = R;
+    if (j < BM - 1 && pos < sm.seg0[e + 1]) al.sorted_rows[pos] = R;
   }
   if (tid == 0) {
     al.seg_start[E] = np;
@@ -568,61 +615,84 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
   if (tid == 0) err_all = 0;
   __syncthreads();
 
-  // Each thread takes kHistBatch rows per pass with all their id loads in
-  // flight before the LDS atomics (a pass per row would pay the global load
-  // latency once per row).
+  // Tokens per adapter rank and rows per (expert, adapter rank) bucket.
+  // Each pass takes up to kHistBatch tokens and kRowBatch rows per thread
+  // and issues all their loads (clamped indices) before the first use, so a
+  // pass pays the global load latency once; the LDS atomics follow.  Slots
+  // past the end for the whole workgroup are skipped by uniform branches
+  // (one workgroup retires about one wave instruction per clock, so dead
+  // slots cost time).
   // Tokens per adapter rank: a wave adds each of its distinct ranks once
   // (a prefill's tokens share a few adapters, and per-lane atomics on one
   // LDS word serialize).
-  constexpr int kHistBatch = 8;
+  // A row's token p / k by a multiply-high: with m = ceil(2^32 / k) the
+  // product's high word is exact while p k < 2^32 (the error p (m - 2^32 / k)
+  // / 2^32 stays below 1 / k).
+  constexpr int kHistBatch = 8, kRowBatch = 16;
+  const bool magic_ok = k > 1 && (unsigned long long)R * (unsigned)k < (1ull << 32);
+  const unsigned kmagic = magic_ok ? (unsigned)(((1ull << 32) + k - 1) / k) : 0u;
+  const int npass = max((T + kHistBatch * kAlignThreads - 1) / (kHistBatch * kAlignThreads),
+                        (R + kRowBatch * kAlignThreads - 1) / (kRowBatch * kAlignThreads));
   int err = 0;
-  for (int t0 = tid; t0 < T; t0 += kHistBatch * kAlignThreads) {
-    int ar[kHistBatch];
+  for (int pass = 0; pass < npass; ++pass) {
+    const int t0 = tid + pass * kHistBatch * kAlignThreads;
+    const int p0 = tid + pass * kRowBatch * kAlignThreads;
+    // live slots (uniform): slot u has a token / row for some thread
+    const int nt = min(kHistBatch, max(0, T - pass * kHistBatch * kAlignThreads + kAlignThreads - 1) /
+                                           kAlignThreads);
+    const int nr = min(kRowBatch, max(0, R - pass * kRowBatch * kAlignThreads + kAlignThreads - 1) /
+                                          kAlignThreads);
+    int ta[kHistBatch], re[kRowBatch], ra[kRowBatch];
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u) {
-      const int t = t0 + u * kAlignThreads;
-      ar[u] = t < T ? adapter_rank(aid, t, NA, err) : -1;
+    for (int u = 0; u < kHistBatch; ++u)
+      ta[u] = (u < nt && aid) ? aid[min(t0 + u * kAlignThreads, T - 1)] : -1;
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      re[u] = ra[u] = -1;
+      if (u >= nr) continue;
+      const int p = min(p0 + u * kAlignThreads, R - 1);
+      const int t = k == 1 ? p : magic_ok ? (int)__umulhi((unsigned)p, kmagic) : p / k;
+      re[u] = ids[p];
+      ra[u] = aid ? aid[t] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kHistBatch; ++u) {
-      unsigned long long active = __ballot(ar[u] >= 0);
+      if (u >= nt) break;
+      const int a = ta[u];
+      const bool live = t0 + u * kAlignThreads < T;
+      if (live && (a < -1 || a >= NA)) err |= MOELORA_DEVERR_ADAPTER_ID;
+      const int ar = !live ? -1 : (a >= 0 && a < NA) ? a : NA;
+      unsigned long long active = __ballot(ar >= 0);
       while (active) {
         const int leader = __ffsll((long long)active) - 1;
-        const int key = __shfl(ar[u], leader);
-        const unsigned long long peers = __ballot(ar[u] == key) & active;
+        const int key = __shfl(ar, leader);
+        const unsigned long long peers = __ballot(ar == key) & active;
         if (lane == leader) atomicAdd(&tok_cnt[key], __popcll(peers));
         active &= ~peers;
       }
     }
-  }
-  constexpr int kRowBatch = 16;
-  for (int p0 = tid; p0 < R; p0 += kRowBatch * kAlignThreads) {
-    int key[kRowBatch];
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u) {
-      const int p = p0 + u * kAlignThreads;
-      key[u] = -1;
-      if (p < R) {
-        const int e = ids[p];
-        int dummy = 0;
-        const int ar = adapter_rank(aid, p / k, NA, dummy);
-        if (e < 0 || e >= E) err |= MOELORA_DEVERR_EXPERT_ID;
-        else key[u] = e * NR + ar;
-      }
+      if (u >= nr) break;
+      if (p0 + u * kAlignThreads >= R) continue;
+      const int e = re[u], a = ra[u];
+      const int ar = (a >= 0 && a < NA) ? a : NA;
+      if (e < 0 || e >= E) err |= MOELORA_DEVERR_EXPERT_ID;
+      else atomicAdd(&sm.hist[e * NR + ar], 1);
     }
-#pragma unroll
-    for (int u = 0; u < kRowBatch; ++u)
-      if (key[u] >= 0) atomicAdd(&sm.hist[key[u]], 1);
   }
   if (err) atomicOr(&err_all, err);
   __syncthreads();
 
   const AlignPlan P = align_plan_wave_ok(s) ? align_plan_wave(s, sm) : align_plan(s, sm);
-  if (tid == 0) {
+  if (wv == 0) {  // start of each adapter rank's tokens: wave scans, 64 ranks at a time
     int run = 0;
-    for (int a = 0; a < NR; ++a) {
-      tok_base[a] = run;
-      run += tok_cnt[a];
+    for (int a0 = 0; a0 < NR; a0 += kWave) {
+      const int a = a0 + lane;
+      int tot;
+      const int x = wave_excl_scan(a < NR ? tok_cnt[a] : 0, &tot);
+      if (a < NR) tok_base[a] = run + x;
+      run += tot;
     }
   }
   __syncthreads();

@@ -32,7 +32,7 @@ inline hipError_t launch_kernel(F kern, dim3 grid, dim3 block, size_t lds, hipSt
 struct Shape {
   int T, H, I, E, k, NA, r;
   int R;      // T * k routed rows
-  int BM;     // rows per block (a multiple of 16)
+  int BM;     // rows per block: 16, 32, 64 or 128 (a power of two)
   int cap;    // upper bound of the padded row count
   int nblk;   // cap / BM
   int max_seg, max_tiles;
