@@ -8,6 +8,10 @@ summaries kept under ``profiles/``:
 * ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (one counter per run):
   HBM bytes per dispatch, scaled by what the same counters report for a
   plain device copy of known size (``<name>_counter_collection.csv``);
+* ``--pmc`` passes of matrix-core, cache and wave counters (names from
+  ``rocprofv3 -L`` on gfx950): MFMA busy cycles against the SIMDs' active
+  cycles, MFMA operations issued, L2 hit rate, L1-to-L2 read latency, LDS
+  bank conflicts and wave waiting time per dispatch;
 * ``--hip-trace --hsa-trace --memory-allocation-trace --kernel-trace`` of
   ``tests/steady_state_child.py``: the HIP and HSA calls, allocations and
   dispatches between the child's two marker calls (steady-state forwards).
@@ -22,6 +26,7 @@ Usage::
     python -m lora_expert_gemm_amd.profiling traffic <workload> <fetch.csv> <write.csv> \
         <copy_fetch.csv> <copy_write.csv> <copy_mib> <traffic.json> <out.md> <source_hash> <command...>
     python -m lora_expert_gemm_amd.profiling steady <trace dir> <out.md> <command...>
+    python -m lora_expert_gemm_amd.profiling mfma <workload> <out.md> <csv>... -- <command...>
 
 The trailing words are the rocprofv3 command(s) that made the CSVs, recorded
 in the summary; a ";;" word separates commands.
@@ -96,7 +101,10 @@ def write_stats_md(workload, stats_csv, out_md, command):
              "Command (run from /tmp with TMPDIR=/tmp):", "", "```", command, "```", "",
              "| kernel | stage | calls | average (us) | share |", "|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| {r['kernel']} | {stage_of(r['kernel']) or '-'} | {r['calls']} | "
+        k = r["kernel"]
+        if stage_of(k) is None and len(k) > 80:  # library kernels: the name's start
+            k = k[:77] + "..."
+        lines.append(f"| {k} | {stage_of(r['kernel']) or '-'} | {r['calls']} | "
                      f"{r['avg_us']:.2f} | {r['share']:.1f}% |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -150,6 +158,58 @@ def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     return entry
+
+
+# gfx950 (MI355X): 8 XCDs of 32 CUs, 4 SIMDs per CU.  GRBM_GUI_ACTIVE is
+# reported summed over the XCDs, SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs.
+N_XCD, N_SIMD = 8, 1024
+MFMA_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "TCC_HIT_sum", "TCC_MISS_sum", "TCP_TCC_READ_REQ_LATENCY_sum",
+                 "TCP_TCC_READ_REQ_sum", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                 "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+
+
+def write_mfma(workload, csvs, out_md, command):
+    """Matrix-core utilisation and memory-side counters per stage."""
+    vals, dur = defaultdict(dict), defaultdict(list)
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = short_name(r["Kernel_Name"])
+                if stage_of(k) is None or r["Counter_Name"] not in MFMA_COUNTERS:
+                    continue
+                vals[k].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    mean = lambda k, c: (sum(vals[k][c]) / len(vals[k][c])) if vals[k].get(c) else None
+    lines = [f"# Matrix-core and memory counters: {workload}", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; one counter set per pass):", "", "```",
+             command, "```", "",
+             f"Per dispatch means.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / "
+             f"{N_XCD} x {N_SIMD} SIMDs); MFMA TFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the "
+             "matrix-core work issued, padding rows and columns included); L2 hit = TCC_HIT / "
+             "(TCC_HIT + TCC_MISS); L1->L2 latency = TCP_TCC_READ_REQ_LATENCY / "
+             "TCP_TCC_READ_REQ (cycles per request); waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES.  "
+             "Durations are those of the counter runs (slower than unprofiled ones).", "",
+             "| stage | kernel | dispatches | MFMA busy | MFMA TFLOP / launch | L2 hit "
+             "| L1->L2 latency | LDS bank conflicts / LDS active | waiting |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    pct = lambda x: "-" if x is None else f"{100 * x:.1f}%"
+    for k in sorted(vals, key=lambda k: -(mean(k, "GRBM_GUI_ACTIVE") or 0)):
+        g, busy = mean(k, "GRBM_GUI_ACTIVE"), mean(k, "SQ_VALU_MFMA_BUSY_CYCLES")
+        mops = mean(k, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        hit, miss = mean(k, "TCC_HIT_sum"), mean(k, "TCC_MISS_sum")
+        lat, req = mean(k, "TCP_TCC_READ_REQ_LATENCY_sum"), mean(k, "TCP_TCC_READ_REQ_sum")
+        bc, la = mean(k, "SQ_LDS_BANK_CONFLICT"), mean(k, "SQ_LDS_IDX_ACTIVE")
+        wa, wc = mean(k, "SQ_WAIT_ANY"), mean(k, "SQ_WAVE_CYCLES")
+        util = busy / (g / N_XCD * N_SIMD) if g and busy is not None else None
+        lines.append(
+            f"| {stage_of(k)} | {k} | {len(vals[k].get('GRBM_GUI_ACTIVE', []))} | {pct(util)} | "
+            f"{'-' if mops is None else f'{mops * 512 / 1e12:.3f}'} | "
+            f"{pct(hit / (hit + miss)) if hit is not None and miss and hit + miss > 0 else '-'} | "
+            f"{'-' if not req else f'{lat / req:.0f}'} | "
+            f"{pct(bc / la) if la else '-'} | {pct(wa / wc) if wc else '-'} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 # Calls that load code or allocate: none may fall between the markers.
@@ -239,6 +299,9 @@ def main(argv):
         return " ".join(words).replace(" ;; ", "\n")
     if argv[0] == "stats":
         write_stats_md(argv[1], argv[2], argv[3], cmd(argv[4:]))
+    elif argv[0] == "mfma":
+        i = argv.index("--")
+        write_mfma(argv[1], argv[3:i], argv[2], cmd(argv[i + 1:]))
     elif argv[0] == "steady":
         write_steady_md(argv[1], argv[2], cmd(argv[3:]))
     elif argv[0] == "traffic":
