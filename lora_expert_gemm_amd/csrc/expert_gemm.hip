@@ -703,26 +703,44 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0
   if constexpr (VEC) {
     if (expand_batched<DT, VEC, ROWZ>(a)) {
       // One contraction step per tile (r <= KS), z already in registers:
-      // the descriptors and B chunks of four tiles are loaded together,
-      // then their MFMAs run in tile order.  Loads are unconditional (a
-      // lane past the rank reads a valid address and its value is zeroed).
-      constexpr int TB = 4;
+      // the descriptors and B chunks of eight tiles are loaded together,
+      // then their MFMAs run in tile order.  32-row blocks of a skewed
+      // many-adapter batch carry up to ~18 tiles, whose expand then ends the
+      // kernel's slowest workgroups; the registers are free (the LDS ring,
+      // not the register file, limits these kernels' occupancy).  Loads are
+      // unconditional (a lane past the rank reads a valid address and its
+      // value is zeroed).
+      constexpr int TB = 8;
       const int kk = kg * EPC, kc = kk < r ? kk : 0;
       const bool kin = kk < r;
       for (int tb = t0; tb < t1; tb += TB) {
-        int4 tl[TB];
+        // The batch's descriptors in one load (lane u % TB holds tile
+        // tb + u % TB), then every B load of the batch, then the MFMAs: two
+        // round trips per batch.  The empty statements read the registers
+        // so that each group of loads is complete before the next step;
+        // otherwise the compiler interleaves per tile (a descriptor's wait
+        // then also waits for the earlier tiles' B loads, and each tile's
+        // loads sink down to its MFMAs past the batch's end test): one round
+        // trip per tile.
+        const int lu = threadIdx.x & (TB - 1);
+        const int4 dl = reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + lu, t1 - 1)];
+        asm volatile("" ::"v"(dl.y), "v"(dl.z), "v"(dl.w));
         u32x4_t c0[TB], c1[TB];
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-          tl[u] = reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + u, t1 - 1)];
-          const DT *b0 = Bbase + (((size_t)tl[u].y * s.E + e) * b_rows + row) * r;
+          const int ad = __builtin_amdgcn_readlane(dl.y, u);
+          const DT *b0 = Bbase + (((size_t)ad * s.E + e) * b_rows + row) * r;
           c0[u] = load_chunk(b0, kc);
           c1[u] = TWO ? load_chunk(b0 + row_off1 * r, kc) : c0[u];
         }
+        static_assert(TB == 8, "one statement reads the whole batch");
+        asm volatile("" ::"v"(c0[0]), "v"(c0[1]), "v"(c0[2]), "v"(c0[3]), "v"(c0[4]), "v"(c0[5]),
+                     "v"(c0[6]), "v"(c0[7]), "v"(c1[0]), "v"(c1[1]), "v"(c1[2]), "v"(c1[3]),
+                     "v"(c1[4]), "v"(c1[5]), "v"(c1[6]), "v"(c1[7]));
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
           if (tb + u >= t1) break;
-          const int lo = tl[u].z, n = tl[u].w;
+          const int lo = __builtin_amdgcn_readlane(dl.z, u), n = __builtin_amdgcn_readlane(dl.w, u);
           const u32x4_t a0 = kin ? c0[u] : u32x4_t{0, 0, 0, 0};
           const u32x4_t a1 = kin ? c1[u] : u32x4_t{0, 0, 0, 0};
 #pragma unroll
