@@ -740,10 +740,18 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_meta(Shape s, const int
 // the bucket's rows, in ascending row order, from its start position.  The
 // rows of adapter rank a are visited token by token in tok_perm order
 // (ascending token), j ascending, so the order is ascending p.
+// With SHRINK, a bucket with an adapter is one LoRA segment, and after
+// placing each chunk of its rows the workgroup computes their gate_up
+// shrink (z = x A_gu[a][e]^T, seg_shrink) -- the shrink rides along with
+// the alignment instead of running as a launch of its own, and reads the
+// segment's A once.
+template <bool SHRINK>
 __global__ __launch_bounds__(kScatterThreads) void k_align_scatter(Shape s,
                                                                    const int *__restrict__ ids,
-                                                                   AlignBufs al) {
+                                                                   AlignBufs al, SegShrinkArgs ss) {
   __shared__ int wsum[kScatterThreads / kWave];
+  __shared__ int crow[SHRINK ? kScatterThreads : 1];                  // x row of each chunk row
+  __shared__ float part[SHRINK ? kScatterThreads / kWave * 256 : 1];  // seg_shrink partials
   const int NR = s.NA + 1;
   const int bucket = blockIdx.x;
   const int e = bucket / NR, ar = bucket % NR;
@@ -754,6 +762,20 @@ __global__ __launch_bounds__(kScatterThreads) void k_align_scatter(Shape s,
   const int k = s.k;
   const int nitems = (t_hi - t_lo) * k;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  // The segment's A rows are known before its rows are: one dword of each
+  // of their 128-byte lines is read now, with the scatter's first loads, so
+  // the shrink finds them in L2 instead of waiting for HBM after the
+  // scatter (the value is only held until the end, never used).
+  uint32_t touch = 0;
+  const uint16_t *Aseg = nullptr;
+  if constexpr (SHRINK) {
+    if (ar < s.NA) {
+      Aseg = static_cast<const uint16_t *>(ss.A) + ((size_t)ar * s.E + e) * s.r * ss.K;
+      const size_t lines = ((size_t)s.r * ss.K * 2 + 127) / 128;
+      for (size_t l = tid; l < lines; l += kScatterThreads)
+        touch ^= *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(Aseg) + 128 * l);
+    }
+  }
   int running = 0;
   for (int c0 = 0; c0 < nitems && running < cnt; c0 += kScatterThreads) {
     const int i = c0 + tid;
@@ -772,10 +794,21 @@ __global__ __launch_bounds__(kScatterThreads) void k_align_scatter(Shape s,
       pre += (w2 < wv) ? wsum[w2] : 0;
       tot += wsum[w2];
     }
-    if (pred) al.sorted_rows[base + running + pre + __popcll(bal & lanemask_lt(lane))] = p;
+    const int slot = pre + __popcll(bal & lanemask_lt(lane));
+    if (pred) al.sorted_rows[base + running + slot] = p;
+    if constexpr (SHRINK) {
+      if (ar < s.NA) {  // (uniform) a LoRA segment
+        if (pred) crow[slot] = p / k;
+        __syncthreads();
+        seg_shrink<kScatterThreads / kWave>(static_cast<const uint16_t *>(ss.x), crow, tot, Aseg,
+                                            ss.K, s.r, ss.z + (size_t)(base + running) * s.r,
+                                            part);
+      }
+    }
     running += tot;
     __syncthreads();
   }
+  if constexpr (SHRINK) asm volatile("" ::"v"(touch));
 }
 
 // Gate_up shrink of routed row p = blockIdx.x - 1, riding along with the
@@ -901,8 +934,10 @@ hipError_t launch_small(const Shape &s, const float *logits, const int *ids, int
 template <int SLOTS>
 hipError_t launch_route_align_t(const Shape &s, const float *logits, const int *ids, int *ids_ws,
                                 float *w_ws, const int *adapter_ids, const AlignBufs &al,
-                                const RowShrinkArgs *rs, bool bf16, hipStream_t st) {
+                                const RowShrinkArgs *rs, const SegShrinkArgs *ss, bool bf16,
+                                hipStream_t st) {
   if (s.R <= kSmallRows) {
+    if (ss) return hipErrorInvalidValue;  // segment shrinks ride along with the scatter only
     if (!rs)
       return launch_small<SLOTS, void>(s, logits, ids, ids_ws, w_ws, adapter_ids, al,
                                        RowShrinkArgs{}, 1, st);
@@ -922,18 +957,21 @@ hipError_t launch_route_align_t(const Shape &s, const float *logits, const int *
   hipError_t e =
       launch_kernel(k_align_meta, dim3(1), dim3(kAlignThreads), 0, st, s, ids, adapter_ids, al);
   if (e != hipSuccess) return e;
-  return launch_kernel(k_align_scatter, dim3(s.E * (s.NA + 1)), dim3(kScatterThreads), 0, st, s,
-                       ids, al);
+  if (ss)
+    return launch_kernel(k_align_scatter<true>, dim3(s.E * (s.NA + 1)), dim3(kScatterThreads), 0, st,
+                         s, ids, al, *ss);
+  return launch_kernel(k_align_scatter<false>, dim3(s.E * (s.NA + 1)), dim3(kScatterThreads), 0, st,
+                       s, ids, al, SegShrinkArgs{});
 }
 
 }  // namespace
 
 hipError_t launch_route_align(const Shape &s, const float *logits, const int *ids,
                               int *ids_ws, float *w_ws, const int *adapter_ids,
-                              const AlignBufs &al, const RowShrinkArgs *rs, bool bf16,
-                              hipStream_t st) {
+                              const AlignBufs &al, const RowShrinkArgs *rs,
+                              const SegShrinkArgs *ss, bool bf16, hipStream_t st) {
 #define MOELORA_RA(SL) \
-  launch_route_align_t<SL>(s, logits, ids, ids_ws, w_ws, adapter_ids, al, rs, bf16, st)
+  launch_route_align_t<SL>(s, logits, ids, ids_ws, w_ws, adapter_ids, al, rs, ss, bf16, st)
   if (s.E <= 64) return MOELORA_RA(1);
   if (s.E <= 128) return MOELORA_RA(2);
   if (s.E <= 256) return MOELORA_RA(4);

@@ -315,6 +315,15 @@ GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora, bool rowz =
   return v;
 }
 
+// Tile-mode LoRA on the streaming GEMMs with the large-batch alignment (a
+// scatter launch): the gate_up shrink rides along with the scatter, one
+// workgroup per LoRA segment, when the layer is bf16 with 16-byte aligned
+// rows and H a multiple of 32; otherwise it runs as its own launch.
+bool fold_gu_shrink(const moelora_desc &d, const Shape &s, int tg, const GemmVariant &vg, bool row) {
+  return !row && tg != kTgTiled && s.R > kSmallRows && vg.bf16 && vg.vec && vg.even_k &&
+         d.n_adapters > 0 && d.rank > 0;
+}
+
 // Row-wise LoRA (decode-sized batches): the shrinks ride along with the
 // routing/alignment launch and the down launch, and the down expand moves
 // into the combine.  Needs the one-workgroup alignment and down workgroups
@@ -479,11 +488,15 @@ moelora_status moelora_plan_info(moelora_plan_t plan, int32_t n_tokens, char *bu
   snprintf(buf, buf_len,
            "dtype=%s block_m=%d tg=%d vec=%d even_k_gu=%d even_k_d=%d k_tail_gu=%d "
            "k_tail_d=%d waves_gu=%d waves_d=%d down_rows=%d down_ksplit=%d lora_mode=%s "
-           "shrink_split=%d shrink_waves=%d tok_share_gu=%d tok_share_d=%d cap=%d workspace=%zu",
+           "shrink_split=%d shrink_waves=%d shrink_gu=%s tok_share_gu=%d tok_share_d=%d cap=%d "
+           "workspace=%zu",
            vg.w8 ? "bf16_fp8w" : vg.bf16 ? "bf16" : "f32", L.s.BM, tg, (int)vg.vec, (int)vg.even_k, (int)vd.even_k,
            k_tail(d, d.hidden), k_tail(d, d.inter), wgu, wd, tg == kTgTiled ? 0 : down_rows,
            ksplit, d.n_adapters == 0 ? "none" : use_row_mode(L.s, true, wd) ? "row" : "tile",
            L.split, plan->shrink_waves ? plan->shrink_waves : choose_shrink_waves(L.s, L.split),
+           d.n_adapters == 0 ? "none"
+           : use_row_mode(L.s, true, wd) ? "routing"
+           : fold_gu_shrink(d, L.s, tg, vg, false) ? "scatter" : "kernel",
            (int)shares(plan, tg, wgu, d.hidden), (int)shares(plan, tg, wd, d.inter), L.s.cap, L.total);
   return MOELORA_OK;
 }
@@ -585,9 +598,11 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
   int *ids_ws = reinterpret_cast<int *>(ws + L.off_ids);
   float *w_ws = reinterpret_cast<float *>(ws + L.off_w);
   RowShrinkArgs rs_gu{x, lora_a_gu, z_gu, adapter_ids, d.hidden, vg.vec};
+  const bool fold_gu = lora && fold_gu_shrink(d, s, tg, vg, row);
+  SegShrinkArgs ss_gu{x, lora_a_gu, z_gu, d.hidden};
   MOELORA_TRY(launch_route_align(s, own_route ? router_logits : nullptr, topk_ids, ids_ws, w_ws,
                                  lora ? adapter_ids : nullptr, al, row ? &rs_gu : nullptr,
-                                 vg.bf16, st));
+                                 fold_gu ? &ss_gu : nullptr, vg.bf16, st));
   const int *ids = own_route ? ids_ws : topk_ids;
   const float *wts = own_route ? w_ws : topk_w;
   MOELORA_TRY(mark());
@@ -615,7 +630,7 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
   g.h = h;
   g.y = reinterpret_cast<float *>(ws + L.off_y);
 
-  if (lora && !row) {
+  if (lora && !row && !fold_gu) {
     GemmArgs a = g;
     a.A = lora_a_gu;
     a.z_out = z_gu;
@@ -634,6 +649,7 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
     a.B = lora_b_gu;
     a.z = z_gu;
     a.z2 = z2_gu;
+    if (fold_gu) a.split = 1;  // the scatter writes z whole
     a.waves = waves_gu;
     // (staggered walks: not for one expert, whose blocks all stream the same
     // rows: the dense 64-token gate_up 82 -> 79 us without)

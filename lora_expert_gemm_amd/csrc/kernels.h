@@ -66,6 +66,15 @@ struct RowShrinkArgs {
   bool vec;                // 16-byte vector loads allowed
 };
 
+// Gate_up shrink of the LoRA segments riding along with the alignment's
+// scatter (larger batches): z[pos][c] = x[row at pos] . A[a][e][c].
+struct SegShrinkArgs {
+  const void *x;           // [T][H] bf16
+  const void *A;           // [NA][E][r][K] bf16
+  float *z;                // [cap][r] (one split)
+  int K;                   // contraction length (H)
+};
+
 // Operands of the expert GEMM kernels.  Pointers are typed void and cast to
 // the element type inside the templates.
 struct GemmArgs {
@@ -136,11 +145,13 @@ constexpr int kShrinkWaves = 16;
 // Routing (when logits is non-null; results to ids_ws / w_ws) and the
 // alignment of the routed rows (caller ids when logits is null).  With rs
 // non-null (small batches only) the same launch also runs the gate_up
-// shrink of every routed row.
+// shrink of every routed row; with ss non-null (more than kSmallRows rows;
+// bf16, 16-byte aligned rows, H a multiple of 32) the scatter computes the
+// gate_up shrink of every LoRA segment.
 hipError_t launch_route_align(const Shape &s, const float *logits, const int *ids,
                               int *ids_ws, float *w_ws, const int *adapter_ids,
-                              const AlignBufs &al, const RowShrinkArgs *rs, bool bf16,
-                              hipStream_t st);
+                              const AlignBufs &al, const RowShrinkArgs *rs,
+                              const SegShrinkArgs *ss, bool bf16, hipStream_t st);
 // Largest routed-row count of the one-workgroup routing + alignment.
 constexpr int kSmallRows = 256;
 

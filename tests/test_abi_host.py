@@ -105,6 +105,24 @@ def test_tuning_switches_are_read_at_plan_time(monkeypatch):
     assert all(_info(forced, T)["block_m"] == "64" for T in (1, 8, 16))
 
 
+@pytest.mark.parametrize("desc,T,where", [
+    (DECODE, 16, "routing"),            # row mode: per-row shrinks in the routing launch
+    (dict(max_tokens=256, hidden=2048, inter=768, n_experts=128, top_k=8, n_adapters=32,
+          rank=16, dtype=lib.BF16), 256, "scatter"),   # tile mode, large alignment: folded
+    (dict(max_tokens=256, hidden=2048, inter=768, n_experts=128, top_k=8, n_adapters=32,
+          rank=16, dtype=lib.F32), 256, "kernel"),     # float: its own launch
+    (dict(max_tokens=256, hidden=2050, inter=768, n_experts=128, top_k=8, n_adapters=32,
+          rank=16, dtype=lib.BF16), 256, "kernel"),    # rows not 16-byte aligned
+    (dict(max_tokens=6400, hidden=2880, inter=2880, n_experts=32, top_k=4, n_adapters=4,
+          rank=64, dtype=lib.BF16), 6400, "kernel"),   # LDS-tiled 128-row blocks
+    (dict(max_tokens=256, hidden=2048, inter=768, n_experts=128, top_k=8, n_adapters=0,
+          rank=0, dtype=lib.BF16), 256, "none"),
+])
+def test_where_the_gate_up_shrink_runs(desc, T, where):
+    """The plan reports which launch computes the gate_up shrink."""
+    assert _info(lib.Plan(**desc), T)["shrink_gu"] == where
+
+
 @pytest.mark.parametrize("desc", [
     DECODE,
     dict(max_tokens=6400, hidden=2880, inter=2880, n_experts=32, top_k=4, n_adapters=4,

@@ -58,6 +58,7 @@ SMALL = [
     (24, 256, 384, 1, 1, 3, 16, "bf16", "uniform_with_none"),   # dense: one expert, top-1, row-wise LoRA
     (300, 256, 384, 1, 1, 3, 16, "bf16", "uniform_with_none"),  # dense, LDS-tiled 128-row blocks
     (20, 96, 160, 1, 1, 2, 8, "f32", "uniform_with_none"),      # dense, float
+    (150, 96, 80, 16, 2, 3, 16, "f32", "uniform_with_none"),    # float, tile-wise LoRA (shrink kernel)
 ]
 
 
@@ -94,6 +95,25 @@ def test_caller_ids_one_expert_and_duplicates(T):
     check_alignment(run.alignment(), oracle.ref_align(ids, d["adapter_ids"], w.E, w.NA,
                                                       run.alignment()["block_m"]))
     check_close(run.out_f32(), oracle_out(w, d, ids, wts.astype(np.float64)), "bf16", "ids")
+
+
+def test_long_lora_segment_shrinks_in_chunks():
+    """Tile-mode gate_up shrink riding along with the alignment scatter: one
+    (expert, adapter) segment of 600 rows (more than the scatter's 512-row
+    chunk), every other row spread over the remaining experts."""
+    w = synth.Workload("segment", T=600, H=128, I=96, E=64, k=2, NA=1, r=16, dtype="bf16",
+                       adapters="uniform", seed=11)
+    d = synth.make_inputs(w)
+    ids = np.zeros((w.T, w.k), np.int32)
+    ids[:, 1] = 1 + np.arange(w.T) % (w.E - 1)
+    wts = np.full((w.T, w.k), 0.5, np.float32)
+    run = Run(w, d, route="ids", ids=ids, wts=wts).forward()
+    info = run.plan.info(w.T)
+    say(f"[parity] long segment: plan {info}")
+    assert "lora_mode=tile" in info and "shrink_gu=scatter" in info
+    check_alignment(run.alignment(), oracle.ref_align(ids, d["adapter_ids"], w.E, w.NA,
+                                                      run.alignment()["block_m"]))
+    check_close(run.out_f32(), oracle_out(w, d, ids, wts.astype(np.float64)), "bf16", "segment")
 
 
 def test_all_base_rows_equal_no_lora_bit_exact():
