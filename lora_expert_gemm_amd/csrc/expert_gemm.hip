@@ -831,15 +831,29 @@ __device__ __forceinline__ int active_groups(const GemmArgs &a, int blk) {
   return n;
 }
 
-// Workgroup -> (block, column tile).  Consecutive logical ids walk the
-// blocks of one column tile, so the blocks of one expert share an XCD.
+// Workgroup -> (block, column tile).  The grid is sized for every block
+// the token count could need, but only the first num_padded / BM blocks
+// hold rows (the rest would exit at once).  Workgroups are dealt round the
+// 8 XCDs (workgroup b on XCD b % 8), so each XCD takes an equal, contiguous
+// share of the live (block, column tile) items, in an order where the
+// blocks of one column tile are consecutive (the blocks of one expert share
+// an XCD and its L2); workgroups past their XCD's share get blk = -1.  (A
+// contiguous split of the whole grid, empty blocks included, gave some
+// XCDs a third more live work than others: the 128-expert gate_up kept all
+// slots busy for only ~60 % of the launch.)  The grid is a multiple of 8.
 struct GemmTile {
   int blk, nt;
 };
-__device__ __forceinline__ GemmTile gemm_tile(int nblk, int bid, int nb) {
-  const int L = xcd_remap(bid, nb);
-  return {L % nblk, L / nblk};
+__device__ __forceinline__ GemmTile gemm_tile(const GemmArgs &a, int bid, int ncols) {
+  constexpr int kXcd = 8;
+  const int nreal = a.al.counts[0] / a.s.BM;
+  const int n = nreal * ncols;
+  const int per = (n + kXcd - 1) / kXcd;
+  const int x = bid % kXcd, j = bid / kXcd, L = x * per + j;
+  if (j >= per || L >= n) return {-1, 0};
+  return {L % nreal, L / nreal};
 }
+__host__ __device__ constexpr int round_up8(int v) { return (v + 7) / 8 * 8; }
 
 // gate_up GEMM + expand + SiLU(gate) * up.  Block rows are the expert's
 // sorted rows; a wave's 16 h-columns n need weight rows n (gate) and I + n
@@ -856,9 +870,10 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   const Shape &s = a.s;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int ri = lane & 15, kg = lane >> 4;
-  const GemmTile gt = gemm_tile(s.nblk, blockIdx.x, gridDim.x);
+  const GemmTile gt = gemm_tile(a, blockIdx.x, (s.I + 16 * a.waves - 1) / (16 * a.waves));
+  if (gt.blk < 0) return;
   const int blk = gt.blk;
-  const int e = a.al.block_expert[blk];  // -1 past the padded rows
+  const int e = a.al.block_expert[blk];
   const int I = s.I, H = s.H;
   const int n0 = (gt.nt * a.waves + wave) * 16;
   // (SH: a wave past the last column still takes part in the workgroup's
@@ -993,7 +1008,7 @@ template <typename DT, int TG, int U, bool VEC, bool EVEN_K, int MODE, bool R2, 
 __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   constexpr int BM = 16 * TG;
   const Shape &s = a.s;
-  int bid = blockIdx.x, nb = gridDim.x;
+  int bid = blockIdx.x;
   if constexpr (MODE == 2) {
     __shared__ float red[256];
     if (bid < a.row_wgs) {
@@ -1006,18 +1021,18 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
       return;
     }
     bid -= a.row_wgs;
-    nb -= a.row_wgs;
   }
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int ri = lane & 15, kg = lane >> 4;
-  const GemmTile gt = gemm_tile(s.nblk, bid, nb);
-  const int blk = gt.blk;
-  const int e = a.al.block_expert[blk];
   const int I = s.I, H = s.H;
   // column tile and contraction split: the tiles of split q follow those of
   // split q - 1; split q takes slabs [q nsl / ksplit, (q + 1) nsl / ksplit)
   const int cols = (R2 ? 32 : 16) * a.waves;
   const int ntn = (H + cols - 1) / cols;
+  const GemmTile gt = gemm_tile(a, bid, ntn * (S > 0 ? a.ksplit : 1));
+  if (gt.blk < 0) return;
+  const int blk = gt.blk;
+  const int e = a.al.block_expert[blk];
   const int ksp = gt.nt / ntn, nt = gt.nt - ksp * ntn;
   int k0 = 0, kn = I;
   if (S > 0 && a.ksplit > 1) {
@@ -1395,7 +1410,7 @@ hipError_t launch_gu(const GemmArgs &a, int ntn, hipStream_t st) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
   }
-  return launch_kernel(kern, dim3(ntn * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
+  return launch_kernel(kern, dim3(round_up8(ntn * a.s.nblk)), dim3(kWave * a.waves), lds, st, a);
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE>
 hipError_t go_gate_up(const GemmArgs &a, hipStream_t st) {
@@ -1441,7 +1456,8 @@ hipError_t launch_d(const GemmArgs &a, int ntn, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   const int ks = S > 0 ? a.ksplit : 1;
-  return launch_kernel(kern, dim3(extra + ntn * ks * a.s.nblk), dim3(kWave * a.waves), lds, st, a);
+  return launch_kernel(kern, dim3(extra + round_up8(ntn * ks * a.s.nblk)), dim3(kWave * a.waves), lds,
+                       st, a);
 }
 template <typename DT, int TG, bool VEC, bool EK, int MODE, bool R2>
 hipError_t go_down_r(const GemmArgs &a, int ntn, hipStream_t st) {
