@@ -133,16 +133,6 @@ template <> struct SplitF32<float> {
   }
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Map the hardware id so that consecutive logical ids share an XCD:
-// XCD x receives the logical range [x * n / 8, (x + 1) * n / 8) of the
-// first 8 * (n / 8) ids; the remainder keeps its id.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  constexpr int kXcd = 8;
-  const int per = n / kXcd;
-  if (bid >= per * kXcd) return bid;
-  return (bid % kXcd) * per + bid / kXcd;
-}
 
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
 

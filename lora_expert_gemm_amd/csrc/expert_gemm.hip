@@ -831,29 +831,6 @@ __device__ __forceinline__ int active_groups(const GemmArgs &a, int blk) {
   return n;
 }
 
-// Workgroup -> (block, column tile).  The grid is sized for every block
-// the token count could need, but only the first num_padded / BM blocks
-// hold rows (the rest would exit at once).  Workgroups are dealt round the
-// 8 XCDs (workgroup b on XCD b % 8), so each XCD takes an equal, contiguous
-// share of the live (block, column tile) items, in an order where the
-// blocks of one column tile are consecutive (the blocks of one expert share
-// an XCD and its L2); workgroups past their XCD's share get blk = -1.  (A
-// contiguous split of the whole grid, empty blocks included, gave some
-// XCDs a third more live work than others: the 128-expert gate_up kept all
-// slots busy for only ~60 % of the launch.)  The grid is a multiple of 8.
-struct GemmTile {
-  int blk, nt;
-};
-__device__ __forceinline__ GemmTile gemm_tile(const GemmArgs &a, int bid, int ncols) {
-  constexpr int kXcd = 8;
-  const int nreal = a.al.counts[0] / a.s.BM;
-  const int n = nreal * ncols;
-  const int per = (n + kXcd - 1) / kXcd;
-  const int x = bid % kXcd, j = bid / kXcd, L = x * per + j;
-  if (j >= per || L >= n) return {-1, 0};
-  return {L % nreal, L / nreal};
-}
-__host__ __device__ constexpr int round_up8(int v) { return (v + 7) / 8 * 8; }
 
 // gate_up GEMM + expand + SiLU(gate) * up.  Block rows are the expert's
 // sorted rows; a wave's 16 h-columns n need weight rows n (gate) and I + n

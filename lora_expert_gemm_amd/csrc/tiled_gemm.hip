@@ -171,11 +171,12 @@ __global__ __launch_bounds__(kTThreads, BK == 32 ? 2 : 1) void k_tiled(GemmArgs 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int li = lane & 31, lh = lane >> 5;
 
-  const int Lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int blk = Lid % s.nblk, nt = Lid / s.nblk;
-  const int e = a.al.block_expert[blk];
-  if (e < 0) return;
   const int I = s.I, H = s.H;
+  const GemmTile gt = gemm_tile(a, blockIdx.x, ((GATE_UP ? I : H) + (GATE_UP ? kTW / 2 : kTW) - 1) /
+                                                   (GATE_UP ? kTW / 2 : kTW));
+  if (gt.blk < 0) return;
+  const int blk = gt.blk, nt = gt.nt;
+  const int e = a.al.block_expert[blk];
   const int K = GATE_UP ? H : I;
   const int n0 = nt * (GATE_UP ? kTW / 2 : kTW);  // first output column of the tile
 
@@ -319,12 +320,13 @@ __global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int li = lane & 31, lh = lane >> 5;
 
-  const int Lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int blk = Lid % s.nblk, nt = Lid / s.nblk;  // blocks vary fastest: concurrent
-                                                     // workgroups share a weight tile
-  const int e = a.al.block_expert[blk];
-  if (e < 0) return;
   const int I = s.I, H = s.H;
+  // blocks vary fastest: concurrent workgroups share a weight tile
+  const GemmTile gt = gemm_tile(a, blockIdx.x, ((GATE_UP ? I : H) + (GATE_UP ? kT8W / 2 : kT8W) - 1) /
+                                                   (GATE_UP ? kT8W / 2 : kT8W));
+  if (gt.blk < 0) return;
+  const int blk = gt.blk, nt = gt.nt;
+  const int e = a.al.block_expert[blk];
   const int K = GATE_UP ? H : I;
   const int n0 = nt * (GATE_UP ? kT8W / 2 : kT8W);
 
@@ -590,7 +592,7 @@ hipError_t go_tiled(const GemmArgs &a, hipStream_t st) {
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  return launch_kernel(kern, dim3(ntn * a.s.nblk), dim3(kTThreads), lds, st, a);
+  return launch_kernel(kern, dim3(round_up8(ntn * a.s.nblk)), dim3(kTThreads), lds, st, a);
 }
 
 template <bool GATE_UP, bool LORA>
@@ -601,7 +603,7 @@ hipError_t go_tiled8(const GemmArgs &a, hipStream_t st) {
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kT8Lds);
   if (err != hipSuccess) return err;
-  return launch_kernel(kern, dim3(ntn * a.s.nblk), dim3(kT8Threads), kT8Lds, st, a);
+  return launch_kernel(kern, dim3(round_up8(ntn * a.s.nblk)), dim3(kT8Threads), kT8Lds, st, a);
 }
 
 template <bool GATE_UP, int BK>
