@@ -103,10 +103,11 @@ int choose_tg(const moelora_desc &d, const Tuning &tu, int T) {
   // tuning sweeps only: a forced streaming block size (1, 2 or 4 groups of 16)
   if (tu.tg) return tu.tg;
   // One expert (a dense layer) at decode size: the grid is one or two blocks
-  // wide, so the 128-row tiled kernel (43 workgroups for a 64-token step of
-  // the 4096 x 11008 MLP: 698 us) and 64-row blocks (274 us) leave most CUs
-  // idle; 32-row blocks stream each weight once per block but fill the chip
-  // (185 us).
+  // wide, so the 128-row tiled kernel leaves most CUs idle (43 workgroups for
+  // a 64-token step of the 4096 x 11008 MLP: 698 us).  Up to 64 rows one
+  // 64-row block reads each weight once (that step 122 -> 116 us against
+  // two 32-row blocks, 111 us with a 4-slot ring); above, 32-row blocks.
+  if (d.n_experts == 1 && rows <= 64) return kTgLarge;
   if (d.n_experts == 1 && rows <= 128) return kTgMid;
   if (tiled_ok(d) && rows >= 64 * ne) return kTgTiled;
   if (rows <= 4 * ne) return kTgSmall;
@@ -313,6 +314,11 @@ GemmVariant variant(const moelora_desc &d, int tg, int K, bool lora, bool rowz =
   v.lora = lora;
   v.rowz = rowz;
   return v;
+}
+
+// A one-expert layer whose rows fit one 64-row streaming block.
+bool dense_one_block(const moelora_desc &d, const Shape &s, int tg) {
+  return d.n_experts == 1 && tg == kTgLarge && s.R <= s.BM;
 }
 
 // Tile-mode LoRA on the streaming GEMMs with the large-batch alignment (a
@@ -651,13 +657,19 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
     a.z2 = z2_gu;
     if (fold_gu) a.split = 1;  // the scatter writes z whole
     a.waves = waves_gu;
-    // (staggered walks: not for one expert, whose blocks all stream the same
-    // rows: the dense 64-token gate_up 82 -> 79 us without)
-    a.rotate = plan->rotate && d.n_experts > 1 && (size_t)d.hidden * weight_bytes(d) % 4096 == 0;
+    // (staggered walks: not for one expert with several blocks, whose blocks
+    // all stream the same rows and meet in L2 when they walk in step: the
+    // dense 64-token gate_up in 32-row blocks 82 -> 79 us without)
+    a.rotate = plan->rotate && (d.n_experts > 1 || s.R <= s.BM) &&
+               (size_t)d.hidden * weight_bytes(d) % 4096 == 0;
     // 16-row blocks' gate_up with shared tokens: a 4-slot ring (the decode
     // step: 143 -> 139 us; 32-row blocks lose a workgroup per CU to it and
     // slow down 6-20 %)
     if (tg == kTgSmall && !plan->slots_forced && shares(plan, tg, waves_gu, d.hidden)) a.slots = 4;
+    // one 64-row block of a one-expert layer: a 4-slot ring too (the dense
+    // 64-token step's gate_up 65 -> 64 us, down 41 -> 38 us)
+    if (dense_one_block(d, s, tg) && !plan->slots_forced && shares(plan, tg, waves_gu, d.hidden))
+      a.slots = 4;
     MOELORA_TRY(tg == kTgTiled ? launch_tiled(a, true, vg, st) : launch_gate_up(a, vg, st));
   }
   MOELORA_TRY(mark());
@@ -681,11 +693,14 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
     a.z = z_d;
     a.z2 = z2_d;
     a.waves = waves_d;
-    a.rotate = plan->rotate && d.n_experts > 1 && (size_t)d.inter * weight_bytes(d) % 4096 == 0;
+    a.rotate = plan->rotate && (d.n_experts > 1 || s.R <= s.BM) &&
+               (size_t)d.inter * weight_bytes(d) % 4096 == 0;
     // E4M3 weights, 16-row blocks with shared tokens: a 4-slot down ring too
     // (the decode step's down 56 -> 53 us; bf16 unchanged by it, 32-row
     // blocks slower)
     if (vd.w8 && tg == kTgSmall && !plan->slots_forced && shares(plan, tg, waves_d, d.inter))
+      a.slots = 4;
+    if (dense_one_block(d, s, tg) && !plan->slots_forced && shares(plan, tg, waves_d, d.inter))
       a.slots = 4;
     if (row) {
       a.rs = RowShrinkArgs{h, lora_a_d, z_d, adapter_ids, d.inter, vd.vec};
