@@ -623,10 +623,14 @@ struct W8Rows {
 };
 
 // Scales of the four weight rows an MFMA output lane holds (rows
-// m + 4 kg .. +3 of a 16-row tile at m), applied to the accumulators.
+// m + 4 kg .. +3 of a 16-row tile at m), applied to the accumulators.  They
+// are loaded before the contraction (row_scales), so the epilogue does not
+// wait for them; a tile past the last row reads the last valid tile's.
+__device__ __forceinline__ float4 row_scales(const float *scale, int kg) {
+  return *reinterpret_cast<const float4 *>(scale + 4 * kg);
+}
 template <int TG>
-__device__ __forceinline__ void scale_rows(const float *scale, int kg, f32x4_t *acc) {
-  const float4 s4 = *reinterpret_cast<const float4 *>(scale + 4 * kg);
+__device__ __forceinline__ void scale_rows(float4 s4, f32x4_t *acc) {
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     acc[tg][0] *= s4.x;
@@ -652,11 +656,15 @@ __device__ __forceinline__ int walk_start8(const GemmArgs &a, int K, int col_til
 // routed row prow[tg]; tile mode (one contraction split), z of sorted
 // position blk * BM + tg * 16 + ri.  Neither depends on the LoRA tile, so
 // they are loaded once, before the base contraction, and their latency
-// hides under it.  A padding row reads row 0 / its own unused position; its
-// value is never selected.
+// hides under it, as does that of the descriptors of the expand's first
+// batch of tiles (lane u % kExpandBatch holds tile t0 + u % kExpandBatch).
+// A padding row reads row 0 / its own unused position; its value is never
+// selected.
+constexpr int kExpandBatch = 8;
 template <typename DT, int TG>
 struct ZRows {
   float v[TG][Elem<DT>::kPerChunk];
+  int4 dl0;
 };
 
 template <typename DT, bool VEC, bool ROWZ>
@@ -665,10 +673,13 @@ __device__ __forceinline__ bool expand_batched(const GemmArgs &a) {
 }
 
 template <typename DT, int TG, bool ROWZ>
-__device__ __forceinline__ void load_zrows(const GemmArgs &a, int blk, int kg, int ri,
-                                           const int *prow, ZRows<DT, TG> &z) {
+__device__ __forceinline__ void load_zrows(const GemmArgs &a, int blk, int t0, int t1, int kg,
+                                           int ri, const int *prow, ZRows<DT, TG> &z) {
   constexpr int EPC = Elem<DT>::kPerChunk;
   const int r = a.s.r, kk = kg * EPC, kc = kk < r ? kk : 0;
+  if (t1 > t0)
+    z.dl0 = reinterpret_cast<const int4 *>(a.al.tiles)[min(t0 + (int)(threadIdx.x & (kExpandBatch - 1)),
+                                                          t1 - 1)];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     const size_t row = ROWZ ? (size_t)(prow[tg] < a.s.R ? prow[tg] : 0)
@@ -710,7 +721,7 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0
       // not the register file, limits these kernels' occupancy).  Loads are
       // unconditional (a lane past the rank reads a valid address and its
       // value is zeroed).
-      constexpr int TB = 8;
+      constexpr int TB = kExpandBatch;
       const int kk = kg * EPC, kc = kk < r ? kk : 0;
       const bool kin = kk < r;
       for (int tb = t0; tb < t1; tb += TB) {
@@ -723,7 +734,8 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0
         // loads sink down to its MFMAs past the batch's end test): one round
         // trip per tile.
         const int lu = threadIdx.x & (TB - 1);
-        const int4 dl = reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + lu, t1 - 1)];
+        const int4 dl =
+            tb == t0 ? zr.dl0 : reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + lu, t1 - 1)];
         asm volatile("" ::"v"(dl.y), "v"(dl.z), "v"(dl.w));
         u32x4_t c0[TB], c1[TB];
 #pragma unroll
@@ -878,7 +890,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
   if (MODE != 0) {
     t0 = a.al.block_tile_start[blk];
     t1 = a.al.block_tile_start[blk + 1];
-    if (expand_batched<DT, VEC, MODE == 2>(a)) load_zrows<DT, TG, MODE == 2>(a, blk, kg, ri, prow, zr);
+    if (expand_batched<DT, VEC, MODE == 2>(a))
+      load_zrows<DT, TG, MODE == 2>(a, blk, t0, t1, kg, ri, prow, zr);
   }
   f32x4_t ag[TG], au[TG];
 #pragma unroll
@@ -910,6 +923,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
       }
       const int c8 = (lane & 7) ^ (lane >> 3);
       const int rot = walk_start8(a, H, gt.nt);
+      const float *sc = a.wscale + (size_t)e * 2 * I + min(n0, I - 16);
+      const float4 sg = row_scales(sc, kg), su = row_scales(sc + I, kg);
       if constexpr (SH) {
         contract_shared8_groups<TG, 2, S>(w8, 16 * c8, 16 * (c8 & 3), static_cast<const uint16_t *>(a.x),
                                           (size_t)H, tok_row, ntg, H, kg, ri, wave, rot, tring,
@@ -921,9 +936,8 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
                                        rot, smem + wave * S * 4096, ag, au);
       }
       // the row scales multiply the base contraction only, before the expand
-      const float *sc = a.wscale + (size_t)e * 2 * I + n0;
-      scale_rows<TG>(sc, kg, ag);
-      scale_rows<TG>(sc + I, kg, au);
+      scale_rows<TG>(sg, ag);
+      scale_rows<TG>(su, au);
     } else {
       const uint16_t *dsrc[4];  // [tile][instruction]
 #pragma unroll
@@ -1042,7 +1056,7 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
   if (MODE == 1) {
     t0 = a.al.block_tile_start[blk];
     t1 = a.al.block_tile_start[blk + 1];
-    if (expand_batched<DT, VEC, false>(a)) load_zrows<DT, TG, false>(a, blk, kg, ri, prow, zr);
+    if (expand_batched<DT, VEC, false>(a)) load_zrows<DT, TG, false>(a, blk, t0, t1, kg, ri, prow, zr);
   }
   f32x4_t acc[TG], acc1[TG];
 #pragma unroll
@@ -1069,6 +1083,8 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
                           ((size_t)e * H + min(m0 + 16 * t + 8 * i + (lane >> 3), H - 1)) * I + k0;
       const int c8 = (lane & 7) ^ (lane >> 3);
       const int rot = walk_start8(a, kn, gt.nt);
+      const float *sc = a.wscale + (size_t)e * H + min(m0, H - (R2 ? 32 : 16));
+      const float4 s0 = row_scales(sc, kg), s1 = R2 ? row_scales(sc + 16, kg) : s0;
       if constexpr (SH) {
         contract_shared8_groups<TG, NW, S>(w8, 16 * c8, 16 * (c8 & 3),
                                            static_cast<const uint16_t *>(a.h) + k0, (size_t)I,
@@ -1080,9 +1096,8 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
                                         reinterpret_cast<const uint16_t *const *>(xr), ntg, kn, kg, ri,
                                         rot, smem + wave * S * NW * 2048, acc, acc1);
       }
-      const float *sc = a.wscale + (size_t)e * H + m0;
-      scale_rows<TG>(sc, kg, acc);
-      if (R2) scale_rows<TG>(sc + 16, kg, acc1);
+      scale_rows<TG>(s0, acc);
+      if (R2) scale_rows<TG>(s1, acc1);
     } else {
       const uint16_t *dsrc[2 * NW];  // [tile][instruction]
 #pragma unroll

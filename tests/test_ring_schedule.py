@@ -225,15 +225,19 @@ def _loops(lines):
     Header=..."); the body is the header block and the member blocks after
     it, then the member blocks laid out before it (a latch placed ahead of
     the header)."""
-    blocks = []   # (label, annotation, lines)
+    blocks = []   # [label, annotation, lines]
     for l in lines:
         m = re.match(r"^(\.LBB\w+):\s*(;.*)?$", l)
         if m:
-            blocks.append((m.group(1), m.group(2) or "", []))
+            blocks.append([m.group(1), m.group(2) or "", []])
+        elif blocks and not blocks[-1][2] and re.match(r"^\s*;", l):
+            # a nested loop's header carries its notes on comment lines of
+            # their own ("Parent Loop ...", then "=>  This Inner Loop Header")
+            blocks[-1][1] += " " + l.strip()
         elif blocks:
             blocks[-1][2].append(l)
     for i, (label, note, _) in enumerate(blocks):
-        if "=>This Inner Loop Header" not in note:
+        if not re.search(r"=>\s*This Inner Loop Header", note):
             continue
         tag = "Header=" + label.lstrip(".")
         member = lambda b: b[0] == label or re.search(re.escape(tag) + r"\b", b[1])
