@@ -724,6 +724,16 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0
       constexpr int TB = kExpandBatch;
       const int kk = kg * EPC, kc = kk < r ? kk : 0;
       const bool kin = kk < r;
+      // z of the lane's rows split into MFMA operands once (a row outside
+      // a tile takes zero, whose split is zero)
+      u32x4_t zh[TG], zl[TG];
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        float z[EPC];
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) z[q] = kin ? zr.v[tg][q] : 0.f;
+        SplitF32<DT>::run(z, zh[tg], zl[tg]);
+      }
       for (int tb = t0; tb < t1; tb += TB) {
         // The batch's descriptors in one load (lane u % TB holds tile
         // tb + u % TB), then every B load of the batch, then the MFMAs: two
@@ -757,18 +767,18 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0
           const u32x4_t a1 = kin ? c1[u] : u32x4_t{0, 0, 0, 0};
 #pragma unroll
           for (int tg = 0; tg < TG; ++tg) {
+            // the tile's rows lo .. lo+n-1 miss this 16-row group: it adds nothing
+            if (lo >= 16 * (tg + 1) || lo + n <= 16 * tg) continue;
             const int local = tg * 16 + ri;
-            const bool in = kin && local >= lo && local < lo + n;
-            float z[EPC];
-#pragma unroll
-            for (int q = 0; q < EPC; ++q) z[q] = in ? zr.v[tg][q] : 0.f;
-            u32x4_t zh, zl;
-            SplitF32<DT>::run(z, zh, zl);
-            M::step(acc0[tg], a0, zh);
-            if (TWO) M::step(acc1[tg], a1, zh);
+            const bool in = local >= lo && local < lo + n;
+            const u32x4_t zero = u32x4_t{0, 0, 0, 0};
+            const u32x4_t h = in ? zh[tg] : zero;
+            M::step(acc0[tg], a0, h);
+            if (TWO) M::step(acc1[tg], a1, h);
             if constexpr (sizeof(DT) == 2) {
-              M::step(acc0[tg], a0, zl);
-              if (TWO) M::step(acc1[tg], a1, zl);
+              const u32x4_t l = in ? zl[tg] : zero;
+              M::step(acc0[tg], a0, l);
+              if (TWO) M::step(acc1[tg], a1, l);
             }
           }
         }
