@@ -1271,34 +1271,58 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, const int *__restrict_
   const int H = s.H;
   if (m0 >= H) return;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < s.k; ++j) {
+  const size_t ys = (size_t)s.R * H;  // stride of the contraction partials
+  if (VEC) {
+    // KB routed rows per batch, their loads issued together (a dropped row
+    // reads the token's first row and adds nothing), then added in
+    // ascending j: one round trip per batch instead of one per row (the
+XX
+    constexpr int KB = 8;
+    for (int j0 = 0; j0 < s.k; j0 += KB) {
+      float4 v[KB];
+      float wt[KB];
+      bool ok[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int j = min(j0 + u, s.k - 1), p = t * s.k + j;
+        const int e = ids[p];
+        ok[u] = j0 + u < s.k && e >= 0 && e < s.E;
+        const int pp = ok[u] ? p : t * s.k;
+        wt[u] = w[pp];
+        v[u] = *reinterpret_cast<const float4 *>(y + (size_t)pp * H + m0);
+      }
+      for (int q = 1; q < ksplit; ++q)
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int pp = ok[u] ? t * s.k + j0 + u : t * s.k;
+          const float4 u4 = *reinterpret_cast<const float4 *>(y + q * ys + (size_t)pp * H + m0);
+          v[u].x += u4.x;
+          v[u].y += u4.y;
+          v[u].z += u4.z;
+          v[u].w += u4.w;
+        }
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+        if (ok[u]) {
+          acc[0] += wt[u] * v[u].x;
+          acc[1] += wt[u] * v[u].y;
+          acc[2] += wt[u] * v[u].z;
+          acc[3] += wt[u] * v[u].w;
+        }
+    }
+  }
+  for (int j = 0; j < (VEC ? 0 : s.k); ++j) {
     const int p = t * s.k + j;
     const int e = ids[p];
     if (e < 0 || e >= s.E) continue;
     const float wj = w[p];
     const float *yr = y + (size_t)p * H + m0;
-    const size_t ys = (size_t)s.R * H;  // stride of the contraction partials
-    if (VEC) {
-      float4 v4 = *reinterpret_cast<const float4 *>(yr);
-      for (int q = 1; q < ksplit; ++q) {
-        const float4 u4 = *reinterpret_cast<const float4 *>(yr + q * ys);
-        v4.x += u4.x;
-        v4.y += u4.y;
-        v4.z += u4.z;
-        v4.w += u4.w;
+    for (int q = 0; q < 4; ++q)
+      if (m0 + q < H) {
+        float v = yr[q];
+        for (int u = 1; u < ksplit; ++u) v += yr[u * ys + q];
+        acc[q] += wj * v;
       }
-      acc[0] += wj * v4.x;
-      acc[1] += wj * v4.y;
-      acc[2] += wj * v4.z;
-      acc[3] += wj * v4.w;
-    } else {
-      for (int q = 0; q < 4; ++q)
-        if (m0 + q < H) {
-          float v = yr[q];
-          for (int u = 1; u < ksplit; ++u) v += yr[u * ys + q];
-          acc[q] += wj * v;
-        }
-    }
   }
   DT *o = out + (size_t)t * H + m0;
   for (int q = 0; q < 4; ++q)
