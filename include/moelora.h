@@ -90,10 +90,12 @@ typedef enum moelora_status {
  * fused-MoE kernel optimizations, second item, routes FP8 MoE layers to a
  * fused path; it gives no quantisation scheme, and one scale per output row
  * is the reading taken here).  Each of w_gate_up / w_down then points at the
- * codes, [E][2I][H] / [E][H][I] bytes, followed at the next 256-byte
- * boundary (byte offset round_up(E*2I*H, 256) / round_up(E*H*I, 256)) by the
- * scales, float32 [E][2I] / [E][H].  Requires H and I multiples of 64 and r
- * a multiple of 8. */
+ * codes, [E][2I] rows of H codes / [E][H] rows of I codes, each row padded
+ * with zero bytes to a multiple of 128 bytes (row pitch P = round_up(H, 128)
+ * / round_up(I, 128), so every row starts on a 128-byte line), followed at
+ * the next 256-byte boundary (byte offset round_up(E*2I*P, 256) /
+ * round_up(E*H*P, 256)) by the scales, float32 [E][2I] / [E][H].  Requires H
+ * and I multiples of 64 and r a multiple of 8. */
 typedef enum moelora_dtype {
     MOELORA_F32 = 0,
     MOELORA_BF16 = 1,

@@ -91,10 +91,16 @@ _lib.moelora_timing_end.restype = ctypes.c_int
 
 def fp8_weight_buffer(codes, scales):
     """The weight-buffer layout of MOELORA_BF16_FP8W as a numpy uint8 array:
-    the E4M3 codes ([E][rows][K] bytes), zero bytes up to the next 256-byte
-    boundary, then the float32 row scales ([E][rows])."""
+    the E4M3 codes ([E][rows][K] bytes), each row padded with zero bytes to a
+    multiple of 128 bytes, zero bytes up to the next 256-byte boundary, then
+    the float32 row scales ([E][rows])."""
     import numpy as np
-    c = np.ascontiguousarray(codes, np.uint8).reshape(-1)
+    codes = np.asarray(codes, np.uint8)
+    K = codes.shape[-1]
+    pitch = (K + 127) // 128 * 128
+    c = np.zeros(codes.shape[:-1] + (pitch,), np.uint8)
+    c[..., :K] = codes
+    c = c.reshape(-1)
     sc = np.ascontiguousarray(scales, np.float32).reshape(-1).view(np.uint8)
     off = (c.size + 255) // 256 * 256
     out = np.zeros(off + sc.size, np.uint8)

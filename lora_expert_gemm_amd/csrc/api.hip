@@ -651,7 +651,8 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
     a.W = w_gate_up;
     if (vg.w8)
       a.wscale = reinterpret_cast<const float *>(
-          static_cast<const char *>(w_gate_up) + scale_offset((size_t)d.n_experts * 2 * d.inter * d.hidden));
+          static_cast<const char *>(w_gate_up) +
+          scale_offset((size_t)d.n_experts * 2 * d.inter * row_pitch8(d.hidden)));
     a.B = lora_b_gu;
     a.z = z_gu;
     a.z2 = z2_gu;
@@ -688,7 +689,8 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
     a.W = w_down;
     if (vd.w8)
       a.wscale = reinterpret_cast<const float *>(
-          static_cast<const char *>(w_down) + scale_offset((size_t)d.n_experts * d.hidden * d.inter));
+          static_cast<const char *>(w_down) +
+          scale_offset((size_t)d.n_experts * d.hidden * row_pitch8(d.inter)));
     a.B = lora_b_d;
     a.z = z_d;
     a.z2 = z2_d;

@@ -927,9 +927,9 @@ __global__ __launch_bounds__(256) void k_gate_up(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint8_t *g = static_cast<const uint8_t *>(a.W) +
-                           ((size_t)e * 2 * I + min(n0 + 8 * i + (lane >> 3), I - 1)) * H;
+                           ((size_t)e * 2 * I + min(n0 + 8 * i + (lane >> 3), I - 1)) * row_pitch8(H);
         w8[i] = g;
-        w8[2 + i] = g + (size_t)I * H;
+        w8[2 + i] = g + (size_t)I * row_pitch8(H);
       }
       const int c8 = (lane & 7) ^ (lane >> 3);
       const int rot = walk_start8(a, H, gt.nt);
@@ -1090,7 +1090,8 @@ __global__ __launch_bounds__(256) void k_down(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
           w8[2 * t + i] = static_cast<const uint8_t *>(a.W) +
-                          ((size_t)e * H + min(m0 + 16 * t + 8 * i + (lane >> 3), H - 1)) * I + k0;
+                          ((size_t)e * H + min(m0 + 16 * t + 8 * i + (lane >> 3), H - 1)) *
+                              row_pitch8(I) + k0;
       const int c8 = (lane & 7) ^ (lane >> 3);
       const int rot = walk_start8(a, kn, gt.nt);
       const float *sc = a.wscale + (size_t)e * H + min(m0, H - (R2 ? 32 : 16));

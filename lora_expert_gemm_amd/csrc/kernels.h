@@ -133,6 +133,9 @@ __device__ __forceinline__ GemmTile gemm_tile(const GemmArgs &a, int bid, int nc
   return {L % nreal, L / nreal};
 }
 __host__ __device__ constexpr int round_up8(int v) { return (v + 7) / 8 * 8; }
+// Row pitch in bytes of E4M3 base weights with contraction length K: rows
+// start on 128-byte lines, so each 128-wide slab of a row is one whole line.
+__host__ __device__ constexpr size_t row_pitch8(int K) { return (size_t)(K + 127) / 128 * 128; }
 
 // LDS ring slots per wave of the streaming GEMMs' weight stream (bf16 with a
 // contraction that is a multiple of 64); the launchers hold instances for
