@@ -66,6 +66,10 @@ struct moelora_plan_s {
   int slots = kRingSlots;  // streaming GEMMs: LDS ring slots of the weight stream (0: registers)
   bool slots_forced = false;  // slots set by the caller's environment
   bool rotate = true;      // streaming GEMMs: staggered slab walks for 4 KB-multiple weight rows
+  // LDS-tiled GEMMs: column tiles per group of the item order (<= 1: none).
+  // The 6400-token prefill: 1947 -> 1912 us with 3 (gate_up 1111 -> 1070,
+  // down 640 -> 622; 2: 1922, 4: 1924, 6: 1981).
+  int group = 3;
   int shrink_waves = 0;    // waves per shrink workgroup (0: by tile count)
   // stage timing
   bool timing = false;
@@ -415,6 +419,7 @@ moelora_status moelora_plan(const moelora_desc *desc, moelora_plan_t *plan,
     p->slots_forced = true;
   }
   if (const char *v = getenv("MOELORA_ROTATE")) p->rotate = atoi(v) != 0;
+  if (const char *v = getenv("MOELORA_GROUP")) p->group = std::max(0, std::min(16, atoi(v)));
   if (const char *v = getenv("MOELORA_SHRINK_WAVES"))
     p->shrink_waves = atoi(v) == 4 || atoi(v) == 8 || atoi(v) == kShrinkWaves ? atoi(v) : 0;
   // The largest layout over every token count up to max_tokens.  Sizes are
@@ -627,6 +632,7 @@ moelora_status forward_impl(moelora_plan_t plan, int32_t n_tokens, const void *x
                  ? L.ksplit
                  : 1;
   g.zero_row = ws + L.off_zero;
+  g.group = plan->group;
   const bool t8 = tg == kTgTiled;
   const int z2_gu = lora && t8 && fused_lora_ok(d, d.hidden);
   const int z2_d = lora && t8 && fused_lora_ok(d, d.inter);

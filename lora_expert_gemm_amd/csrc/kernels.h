@@ -100,6 +100,7 @@ struct GemmArgs {
                            // writing its own partial y (1: none)
   int tok_share;           // LDS ring, 4-wave workgroups: the block's tokens fetched
                            // once per workgroup into a shared LDS ring (0: per wave)
+  int group;               // LDS-tiled GEMMs: column tiles per group of the item order (<= 1: none)
   int rotate;              // LDS ring: workgroups start their contraction walk at staggered
                            // slabs (weight rows a multiple of 4 KB), 0: all at slab 0
   int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
@@ -131,6 +132,29 @@ __device__ __forceinline__ GemmTile gemm_tile(const GemmArgs &a, int bid, int nc
   const int x = bid % kXcd, j = bid / kXcd, L = x * per + j;
   if (j >= per || L >= n) return {-1, 0};
   return {L % nreal, L / nreal};
+}
+// The LDS-tiled GEMMs (one workgroup per CU, 32 per XCD at a time) order
+// the items in groups of G column tiles instead (GemmArgs::group = G > 1):
+// group g holds column tiles gG .. gG+G-1 (the last group what is left),
+// its items ordered by block, then column tile.  The workgroups an XCD runs
+// at once then cover about 32 / G blocks x G column tiles: each weight tile
+// is shared through L2 by the blocks of its expert, and each block's token
+// rows by G column tiles (block-major order shares the weights only, column
+// tile-major order the tokens only).
+__device__ __forceinline__ GemmTile gemm_tile_grouped(const GemmArgs &a, int bid, int ncols, int G) {
+  constexpr int kXcd = 8;
+  const int nreal = a.al.counts[0] / a.s.BM;
+  const int n = nreal * ncols;
+  const int per = (n + kXcd - 1) / kXcd;
+  const int x = bid % kXcd, j = bid / kXcd, L = x * per + j;
+  if (j >= per || L >= n) return {-1, 0};
+  const int full = ncols / G, Lf = full * G * nreal;
+  if (L < Lf) {
+    const int g = L / (G * nreal), r = L - g * G * nreal;
+    return {r / G, g * G + r % G};
+  }
+  const int Gw = ncols - full * G, r = L - Lf;
+  return {r / Gw, full * G + r % Gw};
 }
 __host__ __device__ constexpr int round_up8(int v) { return (v + 7) / 8 * 8; }
 // Row pitch in bytes of E4M3 base weights with contraction length K: rows

@@ -172,8 +172,9 @@ __global__ __launch_bounds__(kTThreads, BK == 32 ? 2 : 1) void k_tiled(GemmArgs 
   const int li = lane & 31, lh = lane >> 5;
 
   const int I = s.I, H = s.H;
-  const GemmTile gt = gemm_tile(a, blockIdx.x, ((GATE_UP ? I : H) + (GATE_UP ? kTW / 2 : kTW) - 1) /
-                                                   (GATE_UP ? kTW / 2 : kTW));
+  const int ncols_t = ((GATE_UP ? I : H) + (GATE_UP ? kTW / 2 : kTW) - 1) / (GATE_UP ? kTW / 2 : kTW);
+  const GemmTile gt = a.group > 1 ? gemm_tile_grouped(a, blockIdx.x, ncols_t, a.group)
+                                  : gemm_tile(a, blockIdx.x, ncols_t);
   if (gt.blk < 0) return;
   const int blk = gt.blk, nt = gt.nt;
   const int e = a.al.block_expert[blk];
@@ -322,8 +323,9 @@ __global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
 
   const int I = s.I, H = s.H;
   // blocks vary fastest: concurrent workgroups share a weight tile
-  const GemmTile gt = gemm_tile(a, blockIdx.x, ((GATE_UP ? I : H) + (GATE_UP ? kT8W / 2 : kT8W) - 1) /
-                                                   (GATE_UP ? kT8W / 2 : kT8W));
+  const int ncols_t = ((GATE_UP ? I : H) + (GATE_UP ? kT8W / 2 : kT8W) - 1) / (GATE_UP ? kT8W / 2 : kT8W);
+  const GemmTile gt = a.group > 1 ? gemm_tile_grouped(a, blockIdx.x, ncols_t, a.group)
+                                  : gemm_tile(a, blockIdx.x, ncols_t);
   if (gt.blk < 0) return;
   const int blk = gt.blk, nt = gt.nt;
   const int e = a.al.block_expert[blk];

@@ -481,6 +481,33 @@ def test_fp8_weights(T, H, I, E, k, NA, r, ad):
     say(f"[parity] max_rel={mr:.3e} fro_rel={fr:.3e}")
 
 
+GROUPED = [  # LDS-tiled shapes: (T, H, I, E, k, NA, r)
+    (300, 256, 320, 4, 2, 3, 16),   # 4-wave tiled, partial column tile
+    (400, 128, 256, 2, 2, 5, 64),   # 8-wave tiled, LoRA slabs
+    (1200, 256, 1600, 8, 2, 3, 32), # 8-wave tiled, 7 column tiles in groups of 3 (+1)
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,NA,r", GROUPED)
+def test_grouped_item_order(T, H, I, E, k, NA, r, monkeypatch):
+    """The LDS-tiled GEMMs give the same bits whatever order the workgroups
+    take the (block, column tile) items in: none, or groups of 2, 3 or 4
+    column tiles."""
+    w = synth.Workload("grouped", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
+                       adapters="uniform_with_none", seed=T + I)
+    d = synth.make_inputs(w)
+    outs = {}
+    for g in ("0", "2", "3", "4"):
+        monkeypatch.setenv("MOELORA_GROUP", g)
+        run = Run(w, d).forward()
+        assert "tg=8" in run.plan.info(T), run.plan.info(T)
+        outs[g] = run.out.cpu().numpy().copy()
+    rid, rw = oracle.ref_route(d["logits"], k)
+    check_close(Run(w, d).forward().out_f32(), oracle_out(w, d, rid, rw), "bf16", "grouped order")
+    for g, o in outs.items():
+        assert np.array_equal(o, outs["0"]), f"group {g} differs from the plain order"
+
+
 FP8_PATHS = [
     (16, 256, 320, 8, 2, 3, 16),    # 16-row blocks, tail in the down contraction
     (24, 192, 256, 4, 2, 3, 16),    # 32-row blocks, tail in gate_up
