@@ -6,6 +6,7 @@ import ctypes
 import json
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -241,3 +242,23 @@ def test_binding_loads_torch_first():
                          text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+@pytest.mark.parametrize("K", [64, 192, 2880, 4096])
+def test_fp8_weight_buffer_layout(K):
+    """The E4M3 weight buffer as the header lays it out: rows of K codes
+    padded with zero bytes to a multiple of 128 bytes, then the float32 row
+    scales at the next 256-byte boundary."""
+    E, rows = 3, 5
+    rng = np.random.default_rng(K)
+    codes = rng.integers(0, 256, size=(E, rows, K), dtype=np.uint8)
+    scales = rng.random((E, rows), dtype=np.float32)
+    buf = lib.fp8_weight_buffer(codes, scales)
+    pitch = (K + 127) // 128 * 128
+    off = (E * rows * pitch + 255) // 256 * 256
+    assert buf.dtype == np.uint8 and buf.size == off + 4 * E * rows
+    body = buf[:E * rows * pitch].reshape(E, rows, pitch)
+    assert np.array_equal(body[..., :K], codes)
+    assert not body[..., K:].any()
+    assert not buf[E * rows * pitch:off].any()
+    assert np.array_equal(buf[off:].view(np.float32).reshape(E, rows), scales)
