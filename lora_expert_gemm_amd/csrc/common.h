@@ -87,6 +87,10 @@ __device__ __forceinline__ u32x4_t load_chunk(const DT *row, int k) {
 // non-temporal: the weight stream reads each line once, and so marked it
 // streams 10-12 % faster than with the default policy (decode-sized blocks).
 constexpr int kCpolNonTemporal = 2;
+// Third dword of a raw buffer resource (gfx9 family): 32-bit data format,
+// no swizzle, no stride; loads at offsets past num_records return zero and
+// touch no memory.
+constexpr int kBufferWord3 = 0x00020000;
 
 // Chunk of row[k ..) with zeros past `len`, element by element (any
 // alignment).

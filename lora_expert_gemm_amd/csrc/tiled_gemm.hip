@@ -362,6 +362,41 @@ __global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
       src[8 + j] = row + 8 * c;
     }
   }
+  // The same base-slab rows through buffer resources (the expert's weight
+  // rows; x, or the block's h rows): a weight row past the valid columns of
+  // the tile (the last column tile of I = 2880 holds 64 of 256) or a padding
+  // token row gets an offset past its resource's end, so its load fetches
+  // nothing and leaves stale bytes in its LDS row, whose outputs are
+  // dropped.  The loads keep their count per slab.  Only where every
+  // resource is under 2 GB, so that kOut lies past its end.
+  constexpr uint32_t kOut = 0x80000000u;
+  const size_t erows = GATE_UP ? (size_t)2 * I : (size_t)H;
+  const size_t tbytes = GATE_UP ? (size_t)s.T * H * 2 : (size_t)kTM * I * 2;
+  const bool bres = erows * K * 2 < kOut && tbytes < kOut;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(static_cast<const uint16_t *>(a.W)) + (size_t)e * erows * K, (short)0,
+      bres ? (int)(erows * K * 2) : 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t tres = __builtin_amdgcn_make_buffer_rsrc(
+      GATE_UP ? const_cast<void *>(a.x)
+              : static_cast<void *>(static_cast<uint16_t *>(a.h) + (size_t)blk * kTM * I),
+      (short)0, bres ? (int)tbytes : 0, kBufferWord3);
+  uint32_t voff[10];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 64 * wave + 8 * j + lrow;
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int col = n0 + (GATE_UP ? (r & (kT8W / 2 - 1)) : r);
+    const int row = GATE_UP ? (r < kT8W / 2 ? 0 : I) + col : col;  // within the expert
+    voff[j] = col < (GATE_UP ? I : H) ? (uint32_t)(((size_t)row * K + 8 * c) * 2) : kOut;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = 16 * wave + 8 * j + lrow;
+    const int c = (lane & 7) ^ (((kT8W + t) >> 1) & 7);
+    const int p = a.al.sorted_rows[blk * kTM + t];
+    const size_t off = GATE_UP ? (size_t)(p / s.k) * H : (size_t)t * I;
+    voff[8 + j] = p < s.R ? (uint32_t)((off + 8 * c) * 2) : kOut;
+  }
   const int nbase = K / 64;
   // LoRA expand as extra slabs: for LoRA tile (adapter ad, block rows
   // lo .. lo+n-1) the contraction runs over the 2r entries (z hi | z lo) of
@@ -382,6 +417,20 @@ __global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
     unsigned char *st = smem + buf * kT8Stage;
     if (!LORA || ks < nbase) {
       const int k = ks * 64;
+      if (bres) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              wres, (__attribute__((address_space(3))) void *)(st + (64 * wave + 8 * j) * kT8Row), 16,
+              voff[j], 2 * k, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              tres,
+              (__attribute__((address_space(3))) void *)(st + (kT8W + 16 * wave + 8 * j) * kT8Row),
+              16, voff[8 + j], 2 * k, 0, 0);
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) dma(src[j] + k, st + (64 * wave + 8 * j) * kT8Row);
 #pragma unroll
