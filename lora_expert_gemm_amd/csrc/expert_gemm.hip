@@ -657,7 +657,8 @@ __device__ __forceinline__ int walk_start8(const GemmArgs &a, int K, int col_til
 // position blk * BM + tg * 16 + ri.  Neither depends on the LoRA tile, so
 // they are loaded once, before the base contraction, and their latency
 // hides under it, as does that of the descriptors of the expand's first
-// batch of tiles (lane u % kExpandBatch holds tile t0 + u % kExpandBatch).
+// two batches of tiles (lane u % (2 kExpandBatch) holds tile
+// t0 + u % (2 kExpandBatch)).
 // A padding row reads row 0 / its own unused position; its value is never
 // selected.
 constexpr int kExpandBatch = 8;
@@ -678,8 +679,8 @@ __device__ __forceinline__ void load_zrows(const GemmArgs &a, int blk, int t0, i
   constexpr int EPC = Elem<DT>::kPerChunk;
   const int r = a.s.r, kk = kg * EPC, kc = kk < r ? kk : 0;
   if (t1 > t0)
-    z.dl0 = reinterpret_cast<const int4 *>(a.al.tiles)[min(t0 + (int)(threadIdx.x & (kExpandBatch - 1)),
-                                                          t1 - 1)];
+    z.dl0 = reinterpret_cast<const int4 *>(
+        a.al.tiles)[min(t0 + (int)(threadIdx.x & (2 * kExpandBatch - 1)), t1 - 1)];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     const size_t row = ROWZ ? (size_t)(prow[tg] < a.s.R ? prow[tg] : 0)
@@ -744,13 +745,16 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0
         // loads sink down to its MFMAs past the batch's end test): one round
         // trip per tile.
         const int lu = threadIdx.x & (TB - 1);
+        // the first two batches' descriptors came with z (lanes 0 .. 2 TB - 1)
+        const bool pre = tb - t0 < 2 * TB;
+        const int lb = tb == t0 ? 0 : pre ? TB : 0;  // lane of the batch's first tile
         const int4 dl =
-            tb == t0 ? zr.dl0 : reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + lu, t1 - 1)];
+            pre ? zr.dl0 : reinterpret_cast<const int4 *>(a.al.tiles)[min(tb + lu, t1 - 1)];
         asm volatile("" ::"v"(dl.y), "v"(dl.z), "v"(dl.w));
         u32x4_t c0[TB], c1[TB];
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-          const int ad = __builtin_amdgcn_readlane(dl.y, u);
+          const int ad = __builtin_amdgcn_readlane(dl.y, lb + u);
           const DT *b0 = Bbase + (((size_t)ad * s.E + e) * b_rows + row) * r;
           c0[u] = load_chunk(b0, kc);
           c1[u] = TWO ? load_chunk(b0 + row_off1 * r, kc) : c0[u];
@@ -762,7 +766,8 @@ __device__ __forceinline__ void expand(const GemmArgs &a, int blk, int e, int t0
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
           if (tb + u >= t1) break;
-          const int lo = __builtin_amdgcn_readlane(dl.z, u), n = __builtin_amdgcn_readlane(dl.w, u);
+          const int lo = __builtin_amdgcn_readlane(dl.z, lb + u),
+                    n = __builtin_amdgcn_readlane(dl.w, lb + u);
           const u32x4_t a0 = kin ? c0[u] : u32x4_t{0, 0, 0, 0};
           const u32x4_t a1 = kin ? c1[u] : u32x4_t{0, 0, 0, 0};
 #pragma unroll
