@@ -100,7 +100,8 @@ struct GemmArgs {
                            // writing its own partial y (1: none)
   int tok_share;           // LDS ring, 4-wave workgroups: the block's tokens fetched
                            // once per workgroup into a shared LDS ring (0: per wave)
-  int group;               // LDS-tiled GEMMs: column tiles per group of the item order (<= 1: none)
+  int group;               // LDS-tiled GEMMs: item order, < 0 expert-major, else column tiles
+                           // per group (<= 1: none)
   int rotate;              // LDS ring: workgroups start their contraction walk at staggered
                            // slabs (weight rows a multiple of 4 KB), 0: all at slab 0
   int z2;                  // z / z_out hold bf16 rows [cap][2r] = (hi | lo) of the fp32 shrink
@@ -155,6 +156,23 @@ __device__ __forceinline__ GemmTile gemm_tile_grouped(const GemmArgs &a, int bid
   }
   const int Gw = ncols - full * G, r = L - Lf;
   return {r / Gw, full * G + r % Gw};
+}
+// Expert-major order (GemmArgs::group < 0): an expert's items sit
+// together, column tile outer and block inner, so the blocks that share a
+// weight tile are consecutive items (the XCD runs them at about the same
+// time); an expert's first block is seg_start[e] / BM.
+__device__ __forceinline__ GemmTile gemm_tile_expert(const GemmArgs &a, int bid, int ncols) {
+  constexpr int kXcd = 8;
+  const int BM = a.s.BM;
+  const int nreal = a.al.counts[0] / BM;
+  const int n = nreal * ncols;
+  const int per = (n + kXcd - 1) / kXcd;
+  const int x = bid % kXcd, j = bid / kXcd, L = x * per + j;
+  if (j >= per || L >= n) return {-1, 0};
+  const int e = a.al.block_expert[L / ncols];  // a block of the item's expert
+  const int fb = a.al.seg_start[e] / BM, nb = a.al.seg_start[e + 1] / BM - fb;
+  const int r = L - fb * ncols;
+  return {fb + r % nb, r / nb};
 }
 __host__ __device__ constexpr int round_up8(int v) { return (v + 7) / 8 * 8; }
 // Row pitch in bytes of E4M3 base weights with contraction length K: rows

@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kTThreads, BK == 32 ? 2 : 1) void k_tiled(GemmArgs 
 
   const int I = s.I, H = s.H;
   const int ncols_t = ((GATE_UP ? I : H) + (GATE_UP ? kTW / 2 : kTW) - 1) / (GATE_UP ? kTW / 2 : kTW);
-  const GemmTile gt = a.group > 1 ? gemm_tile_grouped(a, blockIdx.x, ncols_t, a.group)
+  const GemmTile gt = a.group < 0 ? gemm_tile_expert(a, blockIdx.x, ncols_t) : a.group > 1 ? gemm_tile_grouped(a, blockIdx.x, ncols_t, a.group)
                                   : gemm_tile(a, blockIdx.x, ncols_t);
   if (gt.blk < 0) return;
   const int blk = gt.blk, nt = gt.nt;
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
   const int I = s.I, H = s.H;
   // blocks vary fastest: concurrent workgroups share a weight tile
   const int ncols_t = ((GATE_UP ? I : H) + (GATE_UP ? kT8W / 2 : kT8W) - 1) / (GATE_UP ? kT8W / 2 : kT8W);
-  const GemmTile gt = a.group > 1 ? gemm_tile_grouped(a, blockIdx.x, ncols_t, a.group)
+  const GemmTile gt = a.group < 0 ? gemm_tile_expert(a, blockIdx.x, ncols_t) : a.group > 1 ? gemm_tile_grouped(a, blockIdx.x, ncols_t, a.group)
                                   : gemm_tile(a, blockIdx.x, ncols_t);
   if (gt.blk < 0) return;
   const int blk = gt.blk, nt = gt.nt;

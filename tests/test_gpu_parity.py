@@ -491,13 +491,13 @@ GROUPED = [  # LDS-tiled shapes: (T, H, I, E, k, NA, r)
 @pytest.mark.parametrize("T,H,I,E,k,NA,r", GROUPED)
 def test_grouped_item_order(T, H, I, E, k, NA, r, monkeypatch):
     """The LDS-tiled GEMMs give the same bits whatever order the workgroups
-    take the (block, column tile) items in: none, or groups of 2, 3 or 4
-    column tiles."""
+    take the (block, column tile) items in: none, groups of 2, 3 or 4
+    column tiles, or expert-major."""
     w = synth.Workload("grouped", T=T, H=H, I=I, E=E, k=k, NA=NA, r=r, dtype="bf16",
                        adapters="uniform_with_none", seed=T + I)
     d = synth.make_inputs(w)
     outs = {}
-    for g in ("0", "2", "3", "4"):
+    for g in ("0", "2", "3", "4", "-1"):
         monkeypatch.setenv("MOELORA_GROUP", g)
         run = Run(w, d).forward()
         assert "tg=8" in run.plan.info(T), run.plan.info(T)
