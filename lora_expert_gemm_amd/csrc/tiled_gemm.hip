@@ -502,12 +502,13 @@ __global__ __launch_bounds__(kT8Threads, 1) void k_tiled8(GemmArgs a) {
 }
 
 // LoRA shrink for 128-row blocks: z[pos][c] = X[pos] . A[a][e][c] for the
-// rows of one LoRA tile (one workgroup per tile), X = x by token (gate_up)
-// or h by position (down).  A (r <= 64 rows, padded to 64) and the block's
-// 128 token rows are staged through LDS like the GEMM above; wave w takes
-// token tile w against both 32-row halves of A.  Rows outside the tile's
-// run load zeros.  One workgroup covers the whole contraction, so z is
-// final (no partial sums).
+// rows of one LoRA tile, X = x by token (gate_up) or h by position (down).
+// Two workgroups per tile, one per 64-row half of the block (a half without
+// rows of the tile exits at once): A (r <= 64 rows, padded to 64) and the
+// half's token rows are staged through LDS like the GEMM above; wave w
+// takes token tile w % 2 of the half against A rows 32 (w / 2) .. +31.
+// Rows outside the tile's run load zeros.  A workgroup covers the whole
+// contraction, so z is final (no partial sums).
 template <bool FROM_H, int BK, bool EVEN_K>
 __global__ __launch_bounds__(kTThreads) void k_tiled_shrink(GemmArgs a) {
   using L = Lds<BK>;
@@ -517,16 +518,23 @@ __global__ __launch_bounds__(kTThreads) void k_tiled_shrink(GemmArgs a) {
   const Shape &s = a.s;
   const int tile = blockIdx.x;
   if (tile >= a.al.counts[2]) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  // the first tile also clears the zero row that masked expand lanes read
+  if (a.z2 && tile == 0 && blockIdx.y == 0 && tid < 8)
+    reinterpret_cast<u32x4_t *>(a.zero_row)[tid] = u32x4_t{0, 0, 0, 0};
   const int4 tl = reinterpret_cast<const int4 *>(a.al.tiles)[tile];
   const int blk = tl.x, ad = tl.y, lo = tl.z, n = tl.w;
+  // workgroup y takes the tile's rows in block rows r0 .. r0 + kSR - 1
+  constexpr int kSR = kTM / 2;
+  const int r0 = kSR * blockIdx.y;
+  if (lo >= r0 + kSR || lo + n <= r0) return;
   const int e = a.al.block_expert[blk];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int li = lane & 31, lh = lane >> 5;
   const int r = s.r;
   const int K = FROM_H ? s.I : s.H;
 
   constexpr int kRowStep = kTThreads / L::kCpr;
-  constexpr int kALoads = kAR / kRowStep, kBLoads = kTM / kRowStep;
+  constexpr int kALoads = kAR / kRowStep, kBLoads = kSR / kRowStep;
   const int lc = tid % L::kCpr, lr = tid / L::kCpr;
   const uint16_t *arow[kALoads];
 #pragma unroll
@@ -537,7 +545,7 @@ __global__ __launch_bounds__(kTThreads) void k_tiled_shrink(GemmArgs a) {
   bool bok[kBLoads];
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j) {
-    const int rr = lr + j * kRowStep;
+    const int rr = r0 + lr + j * kRowStep;
     const int pos = blk * kTM + rr;
     bok[j] = rr >= lo && rr < lo + n;
     if (FROM_H) {
@@ -569,7 +577,9 @@ __global__ __launch_bounds__(kTThreads) void k_tiled_shrink(GemmArgs a) {
       *reinterpret_cast<u32x4_t *>(sb + L::off(lr + j * kRowStep, lc)) = rb[j];
   };
 
-  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+  // wave: token tile ti (32 rows of the half) against A rows 32 ai .. +31
+  const int ti = wave & 1, ai = wave >> 1;
+  f32x16_t acc = f32x16_t{};
   const int nks = (K + BK - 1) / BK;
   gload(0);
   lstore(0);
@@ -581,57 +591,48 @@ __global__ __launch_bounds__(kTThreads) void k_tiled_shrink(GemmArgs a) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int c = 2 * kk + lh;
-      const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(sa + L::off(li, c));
-      const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(sa + L::off(32 + li, c));
-      const u32x4_t bt = *reinterpret_cast<const u32x4_t *>(sb + L::off(wave * 32 + li, c));
-      mma32(acc[0], a0, bt);
-      mma32(acc[1], a1, bt);
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(sa + L::off(32 * ai + li, c));
+      const u32x4_t bt = *reinterpret_cast<const u32x4_t *>(sb + L::off(32 * ti + li, c));
+      mma32(acc, a0, bt);
     }
     if (ks + 1 < nks) lstore(buf ^ 1);
     __syncthreads();
   }
-  // lane: token column wave*32 + li; A rows 32 i + 8 (v/4) + 4 lh + v%4
-  const int local = wave * 32 + li;
+  // lane: token row r0 + 32 ti + li; A rows 32 ai + 8 (v/4) + 4 lh + v%4
+  const int local = r0 + 32 * ti + li;
   if (a.z2) {
-    // bf16 rows (hi | lo): hi = bf16(z), lo = bf16(z - hi); the first tile
-    // also clears the zero row that masked expand lanes read
-    if (tile == 0 && tid < 8)
-      reinterpret_cast<u32x4_t *>(a.zero_row)[tid] = u32x4_t{0, 0, 0, 0};
+    // bf16 rows (hi | lo): hi = bf16(z), lo = bf16(z - hi)
     if (local < lo || local >= lo + n) return;
     uint16_t *zrow = reinterpret_cast<uint16_t *>(a.z_out) + ((size_t)blk * kTM + local) * 2 * r;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * ai + 8 * g + 4 * lh;
+      if (c >= r) continue;  // r is a multiple of 32 here
+      uint16_t hi[4], lo4[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = 32 * i + 8 * g + 4 * lh;
-        if (c >= r) continue;  // r is a multiple of 32 here
-        uint16_t hi[4], lo4[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float zv = acc[i][4 * g + v];
-          hi[v] = f32_to_bf16(zv);
-          lo4[v] = f32_to_bf16(zv - bf16_to_f32(hi[v]));
-        }
-        *reinterpret_cast<uint2 *>(zrow + c) = __builtin_bit_cast(uint2, hi);
-        *reinterpret_cast<uint2 *>(zrow + r + c) = __builtin_bit_cast(uint2, lo4);
+      for (int v = 0; v < 4; ++v) {
+        const float zv = acc[4 * g + v];
+        hi[v] = f32_to_bf16(zv);
+        lo4[v] = f32_to_bf16(zv - bf16_to_f32(hi[v]));
       }
+      *reinterpret_cast<uint2 *>(zrow + c) = __builtin_bit_cast(uint2, hi);
+      *reinterpret_cast<uint2 *>(zrow + r + c) = __builtin_bit_cast(uint2, lo4);
+    }
     return;
   }
   if (local < lo || local >= lo + n) return;
   float *zrow = a.z_out + ((size_t)blk * kTM + local) * r;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int c = 32 * i + 8 * g + 4 * lh;
-      if (c + 3 < r) {
-        *reinterpret_cast<float4 *>(zrow + c) =
-            make_float4(acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]);
-      } else {
-        for (int v = 0; v < 4; ++v)
-          if (c + v < r) zrow[c + v] = acc[i][4 * g + v];
-      }
+  for (int g = 0; g < 4; ++g) {
+    const int c = 32 * ai + 8 * g + 4 * lh;
+    if (c + 3 < r) {
+      *reinterpret_cast<float4 *>(zrow + c) =
+          make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+    } else {
+      for (int v = 0; v < 4; ++v)
+        if (c + v < r) zrow[c + v] = acc[4 * g + v];
     }
+  }
 }
 
 template <bool GATE_UP, int BK, bool EVEN_K, bool LORA>
@@ -671,7 +672,7 @@ hipError_t launch_tiled_shrink(const GemmArgs &a, bool from_h, hipStream_t st) {
   const int K = from_h ? a.s.I : a.s.H;
   const bool even = K % 64 == 0;
 #define MOELORA_TS(FH, EV) \
-  return launch_kernel(k_tiled_shrink<FH, 64, EV>, dim3(a.s.max_tiles), dim3(kTThreads), 0, st, a)
+  return launch_kernel(k_tiled_shrink<FH, 64, EV>, dim3(a.s.max_tiles, 2), dim3(kTThreads), 0, st, a)
   if (from_h) {
     if (even) MOELORA_TS(true, true);
     MOELORA_TS(true, false);
