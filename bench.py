@@ -384,8 +384,8 @@ def config_of(w, no_lora=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        log(f"bench.py measures one GPU only (every box here has one GPU and this build "
-            f"has no multi-GPU path); --gpus {args.gpus} is not supported")
+        log(f"bench.py measures one GPU only (the layer has no multi-GPU path; how it would "
+            f"shard is described with the design); --gpus {args.gpus} is not supported")
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
